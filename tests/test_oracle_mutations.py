@@ -1,0 +1,135 @@
+"""Planted mistakes in the oracle (on the CPU) must fail at least one pin.
+
+Each mutant below is a plausible slip -- a dropped term, a wrong sign, swapped
+operands, another order or rounding -- patched into the oracle for the span
+of one test; the pin tests are then run against it and must raise.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import test_oracle_adam as pins_adam
+import test_oracle_reduce as pins_reduce
+from oracle import adam, reduce as red
+
+
+def _step(mutation):
+    def step_values(master, m, v, grad, sc):
+        g = adam.grad_f32(grad)
+        b1, b2, c1, c2, eps, step, isb = sc.as_tuple()
+        if mutation == "swap_betas":
+            b1, b2, c1, c2 = b2, b1, c2, c1
+        m_new = b1 * m + c1 * g
+        if mutation == "g_not_squared":
+            v_new = b2 * v + c2 * np.abs(g)
+        else:
+            v_new = b2 * v + c2 * (g * g)
+        if mutation == "eps_inside_sqrt":
+            den = np.sqrt(v_new * isb * isb + eps)
+        elif mutation == "no_v_bias_correction":
+            den = np.sqrt(v_new) + eps
+        else:
+            den = np.sqrt(v_new) * isb + eps
+        upd = step * (m_new / den)
+        if mutation == "old_moment":
+            upd = step * (m / den)
+        th = master + upd if mutation == "wrong_sign" else master - upd
+        return th, m_new, v_new, th.astype(np.float16).view(np.uint16)
+    return step_values
+
+
+ADAM_MUTANTS = ["swap_betas", "g_not_squared", "eps_inside_sqrt", "no_v_bias_correction",
+                "old_moment", "wrong_sign"]
+
+
+@pytest.mark.parametrize("mutation", ADAM_MUTANTS)
+def test_adam_mutants_fail_the_textbook_shadow(monkeypatch, mutation):
+    monkeypatch.setattr(adam, "step_values", _step(mutation))
+    with pytest.raises(AssertionError):
+        for case in [(1e-4, 1e-6, 1e-3, 1e-4, False), (0.0, 0.0, 5e-3, 1e-3, False)]:
+            pins_adam.test_against_fp64_textbook(case)
+
+
+def _scalars(mutation):
+    real = adam.scalars
+
+    def scalars(lr, beta1, beta2, eps, t):
+        sc = real(lr, beta1, beta2, eps, t)
+        if mutation == "no_m_bias_correction":
+            return adam.Scalars(sc.b1, sc.b2, sc.c1, sc.c2, sc.eps, np.float32(lr), sc.isb)
+        if mutation == "one_minus_beta_in_fp32":
+            c1 = np.float32(1.0) - np.float32(beta1)
+            c2 = np.float32(1.0) - np.float32(beta2)
+            return adam.Scalars(sc.b1, sc.b2, c1, c2, sc.eps, sc.step, sc.isb)
+        if mutation == "t_from_zero":
+            return real(lr, beta1, beta2, eps, t + 1)
+        if mutation == "sqrt_not_inverted":
+            return adam.Scalars(sc.b1, sc.b2, sc.c1, sc.c2, sc.eps, sc.step,
+                                np.float32(math.sqrt(1.0 - beta2 ** t)))
+        raise AssertionError(mutation)
+    return scalars
+
+
+@pytest.mark.parametrize("mutation", ["no_m_bias_correction", "one_minus_beta_in_fp32",
+                                      "t_from_zero", "sqrt_not_inverted"])
+def test_scalar_mutants_fail_a_pin(monkeypatch, mutation):
+    monkeypatch.setattr(adam, "scalars", _scalars(mutation))
+    failed = 0
+    for fn in (lambda: pins_adam.test_scalars_against_exact(1e-3, 0.9, 0.999, 1e-8, 1),
+               lambda: pins_adam.test_against_fp64_textbook((1e-4, 1e-6, 1e-3, 1e-4, False)),
+               pins_adam.test_closed_form_constant_gradient):
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
+
+def _reduce(mutation):
+    def reduce_values(rows, nd):
+        rows = np.asarray(rows)
+        x = [rows[k].view(np.float16).astype(np.float32) for k in range(nd)]
+        if mutation == "descending_order":
+            x = x[::-1]
+        if mutation == "start_from_first":
+            acc = x[0].copy()
+            rest = x[1:]
+        else:
+            acc = np.zeros(rows.shape[1], np.float32)
+            rest = x
+        for xk in rest:
+            acc = acc + xk
+        if mutation == "divide":
+            return acc / np.float32(nd)
+        if mutation == "no_scale":
+            return acc
+        if mutation == "pairwise":
+            return np.sum(np.stack(x), axis=0, dtype=np.float32) * red.inv_nd(nd)
+        return acc * red.inv_nd(nd)
+    return reduce_values
+
+
+@pytest.mark.parametrize("mutation", ["descending_order", "start_from_first", "divide",
+                                      "no_scale"])
+def test_reduce_mutants_fail_a_pin(monkeypatch, mutation, golden_dir):
+    monkeypatch.setattr(red, "reduce_values", _reduce(mutation))
+    failed = 0
+    for fn in (lambda: pins_reduce.test_hand_worked_cases(golden_dir),
+               lambda: pins_reduce.test_closed_form(3, 0.01),
+               lambda: pins_reduce.test_closed_form(4, 0.01)):
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
+
+def test_reduce_shard_offset_mutant_fails(monkeypatch):
+    real = red.reduce_shard
+
+    def shifted(psi, nd, rank, off, n, rows, g32, g16=None):
+        return real(psi, nd, rank, off, n, np.roll(rows, 1, axis=1), g32, g16)
+    monkeypatch.setattr(red, "reduce_shard", shifted)
+    with pytest.raises(AssertionError):
+        pins_reduce.test_brute_force_all_ranks(37, 3, 10)
