@@ -25,7 +25,13 @@ def _load():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        # torch (imported above) has mapped its HIP runtime; this library's
+        # libamdhip64.so.7 dependency resolves to it.
         lib = ctypes.CDLL(LIB_PATH)
+        with open("/proc/self/maps") as f:
+            runtimes = {line.split()[-1] for line in f if "libamdhip64" in line}
+        if len(runtimes) > 1:
+            raise RuntimeError(f"two HIP runtimes are mapped: {sorted(runtimes)}")
         u64, u32, vp, ci = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
         lib.zsynth_grad_rows.argtypes = [vp, u64, u32, u64, u32, u32, u64, u64, vp, vp, ci, vp]
         lib.zsynth_grad_rows.restype = ci

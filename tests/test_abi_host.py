@@ -1,0 +1,184 @@
+"""The C ABI on the host (no GPU needed): the library loads and exports every
+symbol include/zero.h declares; its host functions (memory model, geometry,
+scalars) agree with the oracle bit for bit; every argument error is rejected
+before any device work.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import zero_sharded_mixed_bucketed_amd as Z
+from conftest import ROOT
+from oracle import adam as oadam
+from oracle import geometry as ogeo
+from oracle import memory_model as omm
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "zero.h")).read()
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", Z.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (zero_[a-z0-9_]+)", out))
+    declared = set(_declared())
+    assert declared == set(Z.EXPORTS)
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert hasattr(Z.lib, name)
+
+
+def test_memory_model_matches_oracle_and_print():
+    for psi in (1 << 20, 1_400_000_000, 7_500_000_000, 13_000_000_000, 10 ** 11):
+        for nd in (1, 4, 32, 64, 400):
+            for st in range(4):
+                assert Z.memory_model(psi, nd, st) == omm.bytes_per_device(psi, nd, st)
+    assert [round(Z.memory_model(7_500_000_000, 64, s) / 1e9, 1) for s in range(4)] == \
+        [120.0, 31.4, 16.6, 1.9]
+
+
+def test_memory_model_rejects():
+    with pytest.raises(Z.ZeroError):
+        Z.memory_model(100, 0, 0)
+    with pytest.raises(Z.ZeroError):
+        Z.memory_model(100, 4, 4)
+
+
+@pytest.mark.parametrize("psi", [1, 7, 37, 1000, 1 << 20, 7_500_000_000, 10 ** 11])
+@pytest.mark.parametrize("nd", [1, 3, 4, 64, 400])
+def test_geometry_matches_oracle(psi, nd):
+    ranks = range(nd) if nd <= 64 else (0, 1, 137, nd - 1)
+    for r in ranks:
+        g = Z.shard_geometry(psi, nd, r)
+        lo, hi = ogeo.shard_range(psi, nd, r)
+        assert (g.offset, g.len) == (lo, hi - lo)
+
+
+def test_bucket_intersect():
+    g = Z.shard_geometry(100, 4, 1)                 # [25, 50)
+    assert Z.bucket_intersect(g, 0, 10) == (25, 25)
+    assert Z.bucket_intersect(g, 20, 10) == (25, 30)
+    assert Z.bucket_intersect(g, 30, 5) == (30, 35)
+    assert Z.bucket_intersect(g, 40, 60) == (40, 50)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.bucket_intersect(g, 95, 10)
+    assert e.value.code == Z.ZERO_E_RANGE
+
+
+@pytest.mark.parametrize("lr,b1,b2,eps", [(1e-3, 0.9, 0.999, 1e-8), (1e-4, 0.9, 0.999, 1e-8),
+                                          (3e-4, 0.8, 0.95, 1e-6), (1.0, 0.0, 0.5, 1e-3)])
+@pytest.mark.parametrize("t", [1, 2, 3, 7, 10, 20, 1000, 10 ** 6])
+def test_scalars_match_oracle_bits(lr, b1, b2, eps, t):
+    got = np.array(Z.adam_scalars(lr, b1, b2, eps, t), dtype=np.float32)
+    want = np.array(oadam.scalars(lr, b1, b2, eps, t).as_tuple(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("args", [
+    (1e-3, 0.9, 0.999, 1e-8, 0),          # step 0
+    (1e-3, 1.0, 0.999, 1e-8, 1),          # beta1 = 1
+    (1e-3, 0.9, -0.1, 1e-8, 1),           # beta2 < 0
+    (1e-3, 0.9, 0.999, 0.0, 1),           # eps = 0
+    (float("nan"), 0.9, 0.999, 1e-8, 1),  # lr NaN
+    (1e-3, 0.9, 0.999, float("inf"), 1),
+])
+def test_scalars_reject(args):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.adam_scalars(*args)
+    assert e.value.code == Z.ZERO_E_INVAL
+
+
+def _geom(psi=100, nd=4, rank=1, offset=None, length=None):
+    g = Z.Geom()
+    g.psi, g.nd, g.rank = psi, nd, rank
+    ref = Z.shard_geometry(psi, nd, rank) if nd and rank < nd and psi else None
+    g.offset = ref.offset if offset is None and ref else (offset or 0)
+    g.len = ref.len if length is None and ref else (length or 0)
+    return g
+
+
+FAKE = 0x10000     # never dereferenced: every call below is rejected first
+
+
+def _reduce(g, off=25, n=25, slices=FAKE, stride=25, g32=FAKE, g16=None):
+    return Z.lib.zero_reduce_shard(ctypes.byref(g), off, n, slices, stride, g32, g16, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: Z.lib.zero_reduce_shard(None, 0, 1, FAKE, 1, FAKE, None, None), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(nd=0, offset=0, length=0)), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(rank=4, offset=0, length=25)), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(offset=26)), Z.ZERO_E_INVAL),          # geometry mismatch
+    (lambda: _reduce(_geom(length=24)), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(), off=90, n=20), Z.ZERO_E_RANGE),      # beyond psi
+    (lambda: _reduce(_geom(), off=2 ** 64 - 5, n=10), Z.ZERO_E_RANGE),
+    (lambda: _reduce(_geom(), slices=None), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(), g32=None), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(), stride=24), Z.ZERO_E_RANGE),
+    (lambda: _reduce(_geom(), stride=2 ** 63), Z.ZERO_E_RANGE),    # size overflow
+    (lambda: _reduce(_geom(), slices=FAKE + 1), Z.ZERO_E_ALIGN),
+    (lambda: _reduce(_geom(), g32=FAKE + 2), Z.ZERO_E_ALIGN),
+    (lambda: _reduce(_geom(), g16=FAKE + 1), Z.ZERO_E_ALIGN),
+])
+def test_reduce_rejects(call, code):
+    assert call() == code
+    assert Z.last_error()
+
+
+def test_reduce_empty_intersection_is_ok_without_device():
+    # bucket [0, 10) does not meet shard [25, 50): no device call at all
+    assert _reduce(_geom(), off=0, n=10, slices=None, g32=None) == Z.ZERO_OK
+    assert _reduce(_geom(), off=25, n=0) == Z.ZERO_OK
+
+
+def _shard(grad16=0, p16=FAKE, origin=0, plen=100, master=FAKE, grad=FAKE):
+    s = Z.Shard()
+    s.master, s.m, s.v, s.grad = master, FAKE, FAKE, grad
+    s.grad_is_fp16 = grad16
+    s.param16, s.param16_origin, s.param16_len = p16, origin, plen
+    return s
+
+
+def _adam(g, s, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, t=1):
+    return Z.lib.zero_adam_step_shard(ctypes.byref(g), ctypes.byref(s) if s else None, lr, b1,
+                                      b2, eps, t, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _adam(_geom(offset=3), _shard()), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), None), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(), t=0), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(), b1=1.5), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(), eps=-1.0), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(master=None)), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(grad=None)), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(grad16=2)), Z.ZERO_E_INVAL),
+    (lambda: _adam(_geom(), _shard(origin=30, plen=70)), Z.ZERO_E_RANGE),   # slot starts before window
+    (lambda: _adam(_geom(), _shard(origin=0, plen=49)), Z.ZERO_E_RANGE),    # slot ends after it
+    (lambda: _adam(_geom(), _shard(origin=26, plen=10 ** 6)), Z.ZERO_E_RANGE),
+    (lambda: _adam(_geom(), _shard(master=FAKE + 2)), Z.ZERO_E_ALIGN),
+    (lambda: _adam(_geom(), _shard(grad=FAKE + 2)), Z.ZERO_E_ALIGN),
+    (lambda: _adam(_geom(), _shard(grad16=1, grad=FAKE + 1)), Z.ZERO_E_ALIGN),
+    (lambda: _adam(_geom(), _shard(p16=FAKE + 1)), Z.ZERO_E_ALIGN),
+])
+def test_adam_rejects(call, code):
+    assert call() == code
+    assert Z.last_error()
+
+
+def test_adam_empty_trailing_shard_is_ok_without_device():
+    g = Z.shard_geometry(10, 16, 15)        # S = 1: ranks 10..15 own nothing
+    assert g.len == 0
+    assert _adam(g, _shard(master=None, grad=None)) == Z.ZERO_OK
+
+
+def test_one_hip_runtime_in_process():
+    # libzero and the synthetic-input library resolve to torch's HIP runtime
+    from synth import device as sdev
+    sdev._load()
+    assert len(Z.hip_runtimes()) == 1, Z.hip_runtimes()

@@ -1,0 +1,43 @@
+// Launch interfaces of the two device kernels (internal to libzero).
+#ifndef ZERO_KERNELS_H_
+#define ZERO_KERNELS_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zero {
+
+// One bucket (or chunk) of the owner's reduce.  Slice columns c in
+// [c_lo, c_hi) are reduced; output element of column c is out32[c + delta].
+struct ReduceLaunch {
+  const uint16_t* rows;  // row k at rows + k * stride
+  uint64_t stride;
+  uint32_t nd;
+  uint64_t c_lo, c_hi;
+  int64_t delta;
+  float* out32;
+  uint16_t* out16;  // nullable
+  float inv_nd;
+};
+
+// One Adam step over n elements.  p16 (nullable) points at the slot of
+// element 0 in the fp16 parameter window.
+struct AdamLaunch {
+  float* master;
+  float* m;
+  float* v;
+  const void* grad;
+  int grad_is_fp16;
+  uint16_t* p16;
+  uint64_t n;
+  float b1, b2, c1, c2, eps, step, isb;
+};
+
+// Both return hipSuccess or the launch error.  `cus` is the device's compute
+// unit count, used to size grid-stride launches.
+hipError_t launch_reduce(const ReduceLaunch& a, int cus, hipStream_t stream);
+hipError_t launch_adam(const AdamLaunch& a, int cus, hipStream_t stream);
+
+}  // namespace zero
+
+#endif  // ZERO_KERNELS_H_

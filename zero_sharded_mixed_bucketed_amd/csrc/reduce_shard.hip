@@ -1,0 +1,218 @@
+// The owner's reduce of one gradient bucket (guide "ZeRO: particionar estados
+// do treino entre GPUs", section "Como funciona": in stage 2 a gradient is
+// reduced only at the process that owns its partition, then released; card
+// "ZeRO-2", section "Gradient lifecycle").
+//
+// Nd fp16 rows, one per data-parallel rank, are summed element by element in
+// fp32, in ascending rank order starting from +0, and scaled once by RN32(1/Nd).
+// The kernel is HBM-bound (2 Nd bytes read and 4 written per output element,
+// no reuse), so it is built for streaming: each thread owns 8 consecutive
+// columns, reads each row's 8 fp16 values with one 16-byte load (narrower
+// only when the row stride or base rules 16 bytes out), keeps the 8 running
+// sums in registers, and issues the loads of a batch of rows before adding
+// them so that many independent loads are in flight.  A
+// workgroup of 256 threads reads 4 KiB contiguous per row.  Vectorisation is
+// across elements, never across ranks, so each element's additions keep the
+// rank order and the result is bit-exact.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace zero {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCols = 8;     // columns per thread (one 16-byte fp16 load per row)
+constexpr int kBatch = 8;    // rows loaded before they are added
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+__device__ __forceinline__ void add8(float (&acc)[kCols], u32x4 x) {
+  acc[0] = acc[0] + h2f(x.x & 0xFFFFu);
+  acc[1] = acc[1] + h2f(x.x >> 16);
+  acc[2] = acc[2] + h2f(x.y & 0xFFFFu);
+  acc[3] = acc[3] + h2f(x.y >> 16);
+  acc[4] = acc[4] + h2f(x.z & 0xFFFFu);
+  acc[5] = acc[5] + h2f(x.z >> 16);
+  acc[6] = acc[6] + h2f(x.w & 0xFFFFu);
+  acc[7] = acc[7] + h2f(x.w >> 16);
+}
+
+struct Args {
+  const uint16_t* rows;
+  uint64_t stride;
+  uint32_t nd;
+  uint64_t col0;     // first column of group 0 (a multiple of 8)
+  uint64_t ngroups;  // groups of 8 columns
+  uint64_t c_lo, c_hi;
+  int64_t delta;
+  float* out32;
+  uint16_t* out16;
+  float inv;
+  int st32;      // 4: 16-byte stores, 2: 8-byte, 1: 4-byte
+  int st16;      // 8: 16-byte stores, 4: 8-byte, 2: 4-byte, 1: 2-byte
+};
+
+__device__ __forceinline__ void store_full(const Args& a, uint64_t o, const float (&r)[kCols]) {
+  float* p = a.out32 + o;
+  if (a.st32 == 4) {
+    __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{r[4], r[5], r[6], r[7]}, reinterpret_cast<f32x4*>(p + 4));
+  } else if (a.st32 == 2) {
+#pragma unroll
+    for (int e = 0; e < kCols; e += 2)
+      __builtin_nontemporal_store(f32x2{r[e], r[e + 1]}, reinterpret_cast<f32x2*>(p + e));
+  } else {
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) __builtin_nontemporal_store(r[e], p + e);
+  }
+  if (a.out16) {
+    uint16_t* q = a.out16 + o;
+    uint32_t h[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) h[e] = f2h(r[e]);
+    if (a.st16 == 8) {
+      *reinterpret_cast<u32x4*>(q) =
+          u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    } else if (a.st16 == 4) {
+      *reinterpret_cast<u32x2*>(q) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(q + 4) = u32x2{h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    } else if (a.st16 == 2) {
+#pragma unroll
+      for (int e = 0; e < kCols; e += 2)
+        *reinterpret_cast<uint32_t*>(q + e) = h[e] | (h[e + 1] << 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kCols; ++e) q[e] = static_cast<uint16_t>(h[e]);
+    }
+  }
+}
+
+// Loads the 8 fp16 values of one row at columns [c, c + 8) with accesses of
+// kW bytes (16, 8, 4 or 2), the widest the row alignment allows.
+template <int kW>
+__device__ __forceinline__ u32x4 load8(const uint16_t* p) {
+  if constexpr (kW == 16) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  } else if constexpr (kW == 8) {
+    const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const u32x2 b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + 4));
+    return u32x4{a.x, a.y, b.x, b.y};
+  } else if constexpr (kW == 4) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    return u32x4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                 __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = __builtin_nontemporal_load(p + e);
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                 h[6] | (h[7] << 16)};
+  }
+}
+
+template <int kW>
+__global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
+  const uint64_t gi = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (gi >= a.ngroups) return;
+  const uint64_t c = a.col0 + gi * kCols;
+  float acc[kCols];
+#pragma unroll
+  for (int e = 0; e < kCols; ++e) acc[e] = 0.0f;  // +0
+
+  if (c >= a.c_lo && c + kCols <= a.c_hi) {
+    const uint16_t* p = a.rows + c;
+    uint32_t k = 0;
+    for (; k + kBatch <= a.nd; k += kBatch) {
+      u32x4 x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x[u] = load8<kW>(p + (k + u) * a.stride);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) add8(acc, x[u]);
+    }
+    for (; k < a.nd; ++k) add8(acc, load8<kW>(p + k * a.stride));
+    float r[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) r[e] = acc[e] * a.inv;
+    store_full(a, static_cast<uint64_t>(static_cast<int64_t>(c) + a.delta), r);
+    return;
+  }
+
+  // A ragged edge group: element-wise, with the same per-element order of
+  // additions.
+  for (uint32_t k = 0; k < a.nd; ++k) {
+    const uint16_t* row = a.rows + static_cast<uint64_t>(k) * a.stride;
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) {
+      const uint64_t col = c + e;
+      if (col >= a.c_lo && col < a.c_hi) acc[e] = acc[e] + h2f(row[col]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kCols; ++e) {
+    const uint64_t col = c + e;
+    if (col >= a.c_lo && col < a.c_hi) {
+      const float r = acc[e] * a.inv;
+      const uint64_t o = static_cast<uint64_t>(static_cast<int64_t>(col) + a.delta);
+      a.out32[o] = r;
+      if (a.out16) a.out16[o] = static_cast<uint16_t>(f2h(r));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceLaunch& L, int /*cus*/, hipStream_t stream) {
+  Args a;
+  a.rows = L.rows;
+  a.stride = L.stride;
+  a.nd = L.nd;
+  a.c_lo = L.c_lo;
+  a.c_hi = L.c_hi;
+  a.col0 = L.c_lo & ~static_cast<uint64_t>(kCols - 1);
+  a.ngroups = (L.c_hi - a.col0 + kCols - 1) / kCols;
+  a.delta = L.delta;
+  a.out32 = L.out32;
+  a.out16 = L.out16;
+  a.inv = L.inv_nd;
+  // Widest access every row start allows: columns of a group start at a
+  // multiple of 8 elements (16 bytes) from the row start.
+  const uintptr_t ra = reinterpret_cast<uintptr_t>(L.rows) | (2 * L.stride) | 16;
+  const int w = static_cast<int>(ra & (~ra + 1));   // lowest set bit, at most 16
+  // Alignment of the output addresses of full groups: column col0 + 8j maps to
+  // out32 + col0 + delta + 8j, so the alignment class is the same for all.
+  const uint64_t o0 = static_cast<uint64_t>(static_cast<int64_t>(a.col0) + a.delta);
+  const uintptr_t b32 = reinterpret_cast<uintptr_t>(L.out32) + 4 * o0;
+  a.st32 = (b32 % 16 == 0) ? 4 : (b32 % 8 == 0) ? 2 : 1;
+  a.st16 = 1;
+  if (L.out16) {
+    const uintptr_t b16 = reinterpret_cast<uintptr_t>(L.out16) + 2 * o0;
+    a.st16 = (b16 % 16 == 0) ? 8 : (b16 % 8 == 0) ? 4 : (b16 % 4 == 0) ? 2 : 1;
+  }
+  const uint64_t blocks = (a.ngroups + kThreads - 1) / kThreads;
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (w) {
+    case 16: hipLaunchKernelGGL(reduce_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zero

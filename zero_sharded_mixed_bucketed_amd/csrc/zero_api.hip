@@ -1,0 +1,254 @@
+// Host side of libzero: argument validation, shard and bucket geometry, the
+// memory model, fp64 derivation of the Adam scalars, and launches.  Every check
+// runs before the first HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kernels.h"
+#include "zero.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ZERO_OK;
+}
+
+// Compute-unit count of the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) {
+    *cus = 256;
+    return ZERO_OK;
+  }
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+      return fail(ZERO_E_DEVICE, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    if (c <= 0) c = 256;
+    g_cus[dev].store(c, std::memory_order_relaxed);
+  }
+  *cus = c;
+  return ZERO_OK;
+}
+
+void geometry(uint64_t psi, uint32_t nd, uint32_t rank, zero_geom_t* out) {
+  const uint64_t s = psi / nd + (psi % nd != 0);
+  // r * s can exceed psi only for trailing ranks; no overflow since r < nd and
+  // s <= psi / nd + 1.
+  uint64_t lo = static_cast<uint64_t>(rank) * s;
+  uint64_t hi = lo + s;
+  if (lo > psi) lo = psi;
+  if (hi > psi) hi = psi;
+  out->psi = psi;
+  out->nd = nd;
+  out->rank = rank;
+  out->offset = lo;
+  out->len = hi - lo;
+}
+
+int check_geom(const zero_geom_t* g) {
+  if (!g) return fail(ZERO_E_INVAL, "geometry is NULL");
+  if (g->nd == 0 || g->rank >= g->nd || g->psi == 0)
+    return fail(ZERO_E_INVAL, "geometry: need psi > 0, nd > 0 and rank < nd");
+  zero_geom_t want;
+  geometry(g->psi, g->nd, g->rank, &want);
+  if (want.offset != g->offset || want.len != g->len)
+    return fail(ZERO_E_INVAL,
+                "geometry: rank %u of %u over psi=%llu owns [%llu, +%llu), not [%llu, +%llu)",
+                g->rank, g->nd, (unsigned long long)g->psi, (unsigned long long)want.offset,
+                (unsigned long long)want.len, (unsigned long long)g->offset,
+                (unsigned long long)g->len);
+  return ZERO_OK;
+}
+
+int check_bucket(const zero_geom_t* g, uint64_t off, uint64_t len) {
+  if (off > g->psi || len > g->psi - off)
+    return fail(ZERO_E_RANGE, "bucket [%llu, +%llu) leaves the parameter vector (psi=%llu)",
+                (unsigned long long)off, (unsigned long long)len,
+                (unsigned long long)g->psi);
+  return ZERO_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_hparams(double lr, double beta1, double beta2, double eps, uint64_t t) {
+  if (t == 0) return fail(ZERO_E_INVAL, "step counts from 1");
+  if (!isfinite(lr)) return fail(ZERO_E_INVAL, "lr must be finite");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+    return fail(ZERO_E_INVAL, "betas must lie in [0, 1)");
+  if (!(eps > 0.0) || !isfinite(eps)) return fail(ZERO_E_INVAL, "eps must be finite and > 0");
+  return ZERO_OK;
+}
+
+void derive_scalars(double lr, double beta1, double beta2, double eps, uint64_t t,
+                    float out[7]) {
+  const double bc1 = 1.0 - pow(beta1, static_cast<double>(t));
+  const double bc2 = 1.0 - pow(beta2, static_cast<double>(t));
+  out[0] = static_cast<float>(beta1);
+  out[1] = static_cast<float>(beta2);
+  out[2] = static_cast<float>(1.0 - beta1);
+  out[3] = static_cast<float>(1.0 - beta2);
+  out[4] = static_cast<float>(eps);
+  out[5] = static_cast<float>(lr / bc1);
+  out[6] = static_cast<float>(1.0 / sqrt(bc2));
+}
+
+}  // namespace
+
+extern "C" {
+
+double zero_memory_model(uint64_t psi, uint32_t nd, int stage) {
+  if (nd == 0) {
+    fail(ZERO_E_INVAL, "nd must be >= 1");
+    return -1.0;
+  }
+  const double p = static_cast<double>(psi);
+  const double n = static_cast<double>(nd);
+  const double params = 2.0 * p, grads = 2.0 * p, optim = 12.0 * p;
+  ok();
+  switch (stage) {
+    case ZERO_STAGE_DP: return params + grads + optim;
+    case ZERO_STAGE_OS: return params + grads + optim / n;
+    case ZERO_STAGE_OS_G: return params + (grads + optim) / n;
+    case ZERO_STAGE_OS_G_P: return (params + grads + optim) / n;
+    default: fail(ZERO_E_INVAL, "stage must be 0..3"); return -1.0;
+  }
+}
+
+int zero_shard_geometry(uint64_t psi, uint32_t nd, uint32_t rank, zero_geom_t* out) {
+  if (!out) return fail(ZERO_E_INVAL, "out is NULL");
+  if (nd == 0 || rank >= nd || psi == 0)
+    return fail(ZERO_E_INVAL, "need psi > 0, nd > 0 and rank < nd");
+  geometry(psi, nd, rank, out);
+  return ok();
+}
+
+int zero_bucket_intersect(const zero_geom_t* g, uint64_t bucket_offset, uint64_t bucket_len,
+                          uint64_t* lo, uint64_t* hi) {
+  int rc = check_geom(g);
+  if (rc) return rc;
+  if (!lo || !hi) return fail(ZERO_E_INVAL, "lo/hi is NULL");
+  if ((rc = check_bucket(g, bucket_offset, bucket_len))) return rc;
+  uint64_t a = bucket_offset > g->offset ? bucket_offset : g->offset;
+  uint64_t b = bucket_offset + bucket_len;
+  if (b > g->offset + g->len) b = g->offset + g->len;
+  if (b < a) b = a;
+  *lo = a;
+  *hi = b;
+  return ok();
+}
+
+int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t bucket_len,
+                      const uint16_t* slices, uint64_t slice_stride, float* grad32,
+                      uint16_t* grad16, void* hip_stream) {
+  int rc = check_geom(g);
+  if (rc) return rc;
+  if ((rc = check_bucket(g, bucket_offset, bucket_len))) return rc;
+  const uint64_t s_lo = g->offset, s_hi = g->offset + g->len;
+  const uint64_t a = bucket_offset > s_lo ? bucket_offset : s_lo;
+  const uint64_t b = (bucket_offset + bucket_len) < s_hi ? (bucket_offset + bucket_len) : s_hi;
+  if (a >= b) return ok();  // nothing of this bucket is owned here
+  if (!slices || !grad32) return fail(ZERO_E_INVAL, "slices and grad32 must not be NULL");
+  if (slice_stride < bucket_len)
+    return fail(ZERO_E_RANGE, "slice_stride %llu < bucket_len %llu",
+                (unsigned long long)slice_stride, (unsigned long long)bucket_len);
+  if (g->nd > 1 && slice_stride > (UINT64_MAX / 2 - bucket_len) / (g->nd - 1))
+    return fail(ZERO_E_RANGE, "slice buffer size overflows");
+  if (!aligned(slices, 2) || !aligned(grad32, 4) || (grad16 && !aligned(grad16, 2)))
+    return fail(ZERO_E_ALIGN, "slices/grad16 need 2-byte and grad32 4-byte alignment");
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  zero::ReduceLaunch L;
+  L.rows = slices;
+  L.stride = slice_stride;
+  L.nd = g->nd;
+  L.c_lo = a - bucket_offset;
+  L.c_hi = b - bucket_offset;
+  // output index of column c is (bucket_offset + c) - shard offset
+  L.delta = static_cast<int64_t>(bucket_offset) - static_cast<int64_t>(s_lo);
+  L.out32 = grad32;
+  L.out16 = grad16;
+  L.inv_nd = 1.0f / static_cast<float>(g->nd);
+  hipError_t e = zero::launch_reduce(L, cus, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(ZERO_E_DEVICE, "reduce launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int zero_adam_scalars(double lr, double beta1, double beta2, double eps, uint64_t step,
+                      float out[7]) {
+  if (!out) return fail(ZERO_E_INVAL, "out is NULL");
+  int rc = check_hparams(lr, beta1, beta2, eps, step);
+  if (rc) return rc;
+  derive_scalars(lr, beta1, beta2, eps, step, out);
+  return ok();
+}
+
+int zero_adam_step_shard(const zero_geom_t* g, const zero_shard_t* s, double lr, double beta1,
+                         double beta2, double eps, uint64_t step, void* hip_stream) {
+  int rc = check_geom(g);
+  if (rc) return rc;
+  if (!s) return fail(ZERO_E_INVAL, "shard is NULL");
+  if ((rc = check_hparams(lr, beta1, beta2, eps, step))) return rc;
+  if (g->len == 0) return ok();  // an empty trailing shard
+  if (!s->master || !s->m || !s->v || !s->grad)
+    return fail(ZERO_E_INVAL, "master, m, v and grad must not be NULL");
+  if (s->grad_is_fp16 != 0 && s->grad_is_fp16 != 1)
+    return fail(ZERO_E_INVAL, "grad_is_fp16 must be 0 or 1");
+  if (s->param16) {
+    if (g->offset < s->param16_origin || s->param16_len < g->len ||
+        g->offset - s->param16_origin > s->param16_len - g->len)
+      return fail(ZERO_E_RANGE, "slot [%llu, +%llu) lies outside the fp16 window [%llu, +%llu)",
+                  (unsigned long long)g->offset, (unsigned long long)g->len,
+                  (unsigned long long)s->param16_origin, (unsigned long long)s->param16_len);
+  }
+  if (!aligned(s->master, 4) || !aligned(s->m, 4) || !aligned(s->v, 4) ||
+      !aligned(s->grad, s->grad_is_fp16 ? 2 : 4) || (s->param16 && !aligned(s->param16, 2)))
+    return fail(ZERO_E_ALIGN, "fp32 arrays need 4-byte, fp16 arrays 2-byte alignment");
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  float sc[7];
+  derive_scalars(lr, beta1, beta2, eps, step, sc);
+  zero::AdamLaunch L;
+  L.master = s->master;
+  L.m = s->m;
+  L.v = s->v;
+  L.grad = s->grad;
+  L.grad_is_fp16 = s->grad_is_fp16;
+  L.p16 = s->param16 ? s->param16 + (g->offset - s->param16_origin) : nullptr;
+  L.n = g->len;
+  L.b1 = sc[0];
+  L.b2 = sc[1];
+  L.c1 = sc[2];
+  L.c2 = sc[3];
+  L.eps = sc[4];
+  L.step = sc[5];
+  L.isb = sc[6];
+  hipError_t e = zero::launch_adam(L, cus, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(ZERO_E_DEVICE, "adam launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* zero_last_error(void) { return g_err; }
+
+}  // extern "C"
