@@ -12,10 +12,10 @@
 //
 // One pass over HBM: each element's g, th, m, v are read once and th, m, v and
 // the fp16 slot written once (30 bytes per element with an fp32 gradient, 28
-// with fp16).  There is no reuse, so the kernel streams: each thread handles
-// groups of 4 elements with 16-byte loads and stores of every fp32 array,
-// loads of all four inputs are issued before any arithmetic, and the grid
-// strides over the shard with a few waves of workgroups per compute unit.
+// with fp16).  There is no reuse, so the kernel streams with non-temporal
+// hints: each thread owns 4 consecutive elements, loads all four inputs with
+// 16-byte accesses before any arithmetic, and stores the results with 16-byte
+// (fp32) and 8-byte (fp16) accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,9 +26,8 @@
 namespace zero {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVec = 4;            // elements per group
-constexpr int kGroupsPerThread = 2;  // groups a thread keeps in flight per iteration
+constexpr int kThreads = 64;    // one wavefront per workgroup
+constexpr int kVec = 4;         // elements per thread (16-byte accesses of the fp32 arrays)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -100,59 +99,31 @@ __device__ __forceinline__ void store_p16(const Args& a, uint64_t j, const f32x4
   }
 }
 
+// One group of 4 elements per thread and a grid that covers the shard: on
+// MI355X this streams the 4-read/4-write mix faster than a grid-stride loop
+// with fewer, larger workgroups (short-lived wave-sized workgroups keep every
+// CU refilled and the live accesses in one moving window of memory).
 template <bool kG16>
 __global__ void __launch_bounds__(kThreads) adam_vec_kernel(Args a) {
-  const uint64_t nthreads = static_cast<uint64_t>(gridDim.x) * kThreads;
-  uint64_t gi = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  // Main loop: kGroupsPerThread groups per iteration, strided by the grid so
-  // that a wavefront's accesses stay contiguous.
-  for (; gi + (kGroupsPerThread - 1) * nthreads < a.ngroups; gi += kGroupsPerThread * nthreads) {
-    f32x4 g[kGroupsPerThread], th[kGroupsPerThread], m[kGroupsPerThread], v[kGroupsPerThread];
-#pragma unroll
-    for (int u = 0; u < kGroupsPerThread; ++u) {
-      const uint64_t j = (gi + u * nthreads) * kVec;
-      g[u] = load_grad<kG16>(a, j);
-      th[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.master + j));
-      m[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.m + j));
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v + j));
-    }
-#pragma unroll
-    for (int u = 0; u < kGroupsPerThread; ++u) {
-      const uint64_t j = (gi + u * nthreads) * kVec;
-      float t0 = th[u].x, t1 = th[u].y, t2 = th[u].z, t3 = th[u].w;
-      float m0 = m[u].x, m1 = m[u].y, m2 = m[u].z, m3 = m[u].w;
-      float v0 = v[u].x, v1 = v[u].y, v2 = v[u].z, v3 = v[u].w;
-      adam_elem(t0, m0, v0, g[u].x, a.s);
-      adam_elem(t1, m1, v1, g[u].y, a.s);
-      adam_elem(t2, m2, v2, g[u].z, a.s);
-      adam_elem(t3, m3, v3, g[u].w, a.s);
-      const f32x4 tn{t0, t1, t2, t3};
-      __builtin_nontemporal_store(tn, reinterpret_cast<f32x4*>(a.master + j));
-      __builtin_nontemporal_store(f32x4{m0, m1, m2, m3}, reinterpret_cast<f32x4*>(a.m + j));
-      __builtin_nontemporal_store(f32x4{v0, v1, v2, v3}, reinterpret_cast<f32x4*>(a.v + j));
-      store_p16(a, j, tn);
-    }
-  }
-  // Remaining full groups, one at a time.
-  for (; gi < a.ngroups; gi += nthreads) {
-    const uint64_t j = gi * kVec;
-    const f32x4 g = load_grad<kG16>(a, j);
-    f32x4 th = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.master + j));
-    f32x4 m = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.m + j));
-    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v + j));
-    float t0 = th.x, t1 = th.y, t2 = th.z, t3 = th.w;
-    float m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
-    float v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
-    adam_elem(t0, m0, v0, g.x, a.s);
-    adam_elem(t1, m1, v1, g.y, a.s);
-    adam_elem(t2, m2, v2, g.z, a.s);
-    adam_elem(t3, m3, v3, g.w, a.s);
-    const f32x4 tn{t0, t1, t2, t3};
-    __builtin_nontemporal_store(tn, reinterpret_cast<f32x4*>(a.master + j));
-    __builtin_nontemporal_store(f32x4{m0, m1, m2, m3}, reinterpret_cast<f32x4*>(a.m + j));
-    __builtin_nontemporal_store(f32x4{v0, v1, v2, v3}, reinterpret_cast<f32x4*>(a.v + j));
-    store_p16(a, j, tn);
-  }
+  const uint64_t gi = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (gi >= a.ngroups) return;
+  const uint64_t j = gi * kVec;
+  const f32x4 g = load_grad<kG16>(a, j);
+  const f32x4 th = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.master + j));
+  const f32x4 m = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.m + j));
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v + j));
+  float t0 = th.x, t1 = th.y, t2 = th.z, t3 = th.w;
+  float m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
+  float v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+  adam_elem(t0, m0, v0, g.x, a.s);
+  adam_elem(t1, m1, v1, g.y, a.s);
+  adam_elem(t2, m2, v2, g.z, a.s);
+  adam_elem(t3, m3, v3, g.w, a.s);
+  const f32x4 tn{t0, t1, t2, t3};
+  __builtin_nontemporal_store(tn, reinterpret_cast<f32x4*>(a.master + j));
+  __builtin_nontemporal_store(f32x4{m0, m1, m2, m3}, reinterpret_cast<f32x4*>(a.m + j));
+  __builtin_nontemporal_store(f32x4{v0, v1, v2, v3}, reinterpret_cast<f32x4*>(a.v + j));
+  store_p16(a, j, tn);
 }
 
 // Element-wise path: the tail after the last full group, or arrays that
@@ -196,11 +167,10 @@ hipError_t launch_adam(const AdamLaunch& L, int cus, hipStream_t stream) {
   a.st16 = 1;
   if (L.p16) a.st16 = al(L.p16, 8) ? 4 : al(L.p16, 4) ? 2 : 1;
   a.ngroups = a.vec ? L.n / kVec : 0;
-  // A few waves of workgroups per compute unit; the grid strides over the rest.
-  const uint64_t want = (a.ngroups + kThreads - 1) / kThreads;
-  const uint64_t cap = static_cast<uint64_t>(cus) * 8;
   if (a.ngroups) {
-    const unsigned blocks = static_cast<unsigned>(want < cap ? want : cap);
+    const uint64_t want = (a.ngroups + kThreads - 1) / kThreads;
+    if (want > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    const unsigned blocks = static_cast<unsigned>(want);
     if (L.grad_is_fp16)
       hipLaunchKernelGGL(adam_vec_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
     else
@@ -211,7 +181,9 @@ hipError_t launch_adam(const AdamLaunch& L, int cus, hipStream_t stream) {
   const uint64_t first = a.ngroups * kVec;
   if (first < L.n) {
     const uint64_t rest = L.n - first;
+    // the tail (< 4 elements) or a whole misaligned shard: grid-stride over it
     const uint64_t want_s = (rest + kThreads - 1) / kThreads;
+    const uint64_t cap = static_cast<uint64_t>(cus) * 32;
     const unsigned blocks = static_cast<unsigned>(want_s < cap ? want_s : cap);
     if (L.grad_is_fp16)
       hipLaunchKernelGGL(adam_scalar_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a,

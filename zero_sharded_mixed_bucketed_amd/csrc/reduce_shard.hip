@@ -11,7 +11,7 @@
 // only when the row stride or base rules 16 bytes out), keeps the 8 running
 // sums in registers, and issues the loads of a batch of rows before adding
 // them so that many independent loads are in flight.  A
-// workgroup of 256 threads reads 4 KiB contiguous per row.  Vectorisation is
+// workgroup of 128 threads reads 2 KiB contiguous per row.  Vectorisation is
 // across elements, never across ranks, so each element's additions keep the
 // rank order and the result is bit-exact.
 #include <hip/hip_runtime.h>
@@ -24,7 +24,7 @@
 namespace zero {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 constexpr int kCols = 8;     // columns per thread (one 16-byte fp16 load per row)
 constexpr int kBatch = 8;    // rows loaded before they are added
 
