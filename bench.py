@@ -41,8 +41,10 @@ def parse():
                              "tiny-zero2"])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 22,
-                    help="shard elements in the oracle's timed sample")
+    ap.add_argument("--cpu-chunk", type=int, default=1 << 22,
+                    help="shard elements per chunk of the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle work to time on the host (seconds, approximate)")
     ap.add_argument("--check-samples", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (untimed) so that a counter "
@@ -207,7 +209,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, geom, args.cpu_sample)
+        cpu = cpu_baseline(w, geom, args.cpu_chunk, args.cpu_seconds)
 
     step_bytes = red_bytes + adam_bytes
     out = {
@@ -303,33 +305,61 @@ def self_check(w, geom, buckets, grad, master, m, v, param16, idx, steps_done):
             "adam_max_rel_err": rel}
 
 
-def cpu_baseline(w, geom, n_sample):
-    """The oracle on the host, on the first n_sample elements of the shard."""
-    from oracle import adam as oadam
-    from oracle import reduce as ored
+def _oracle_inputs(args):
+    """Seeded inputs of one chunk of the shard for the oracle (host generator)."""
     from synth import gen
-    n = min(n_sample, geom.len)
-    flat = np.arange(geom.offset, geom.offset + n, dtype=np.uint64)
+    w, lo, n = args
+    flat = np.arange(lo, lo + n, dtype=np.uint64)
     th = gen.state_f32(w.seed, gen.KIND_MASTER, flat, w.master.sigma)
     mm = gen.state_f32(w.seed, gen.KIND_M, flat, w.m.sigma, w.m.absolute)
     vv = gen.state_f32(w.seed, gen.KIND_V, flat, w.v.sigma, w.v.absolute)
     if w.fp16_grad:
-        t0 = time.perf_counter()
         g = gen.grad_f16(w.seed, 0, flat, w.grad.sigma, kind=gen.KIND_GRAD_FULL)
-        t_red = 0.0
     else:
-        rows = np.stack([gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
-                         for k in range(w.nd)])
-        t0 = time.perf_counter()
-        g = ored.reduce_values(rows, w.nd)
-        t_red = time.perf_counter() - t0
+        g = np.stack([gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
+                      for k in range(w.nd)])
+    return th, mm, vv, g
+
+
+def _oracle_time(w, inputs):
+    from oracle import adam as oadam
+    from oracle import reduce as ored
+    th, mm, vv, g = inputs
+    t0 = time.perf_counter()
+    if not w.fp16_grad:
+        g = ored.reduce_values(g, w.nd)
     t1 = time.perf_counter()
     oadam.step_values(th, mm, vv, g, oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, 1))
-    t_adam = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline(w, geom, chunk, target_s):
+    """The oracle on the host, single-threaded, over consecutive chunks of the shard
+    until about target_s seconds of oracle work (inputs are generated first, in a
+    worker pool, and are not timed)."""
+    import multiprocessing as mp
+    first = _oracle_inputs((w, geom.offset, min(chunk, geom.len)))
+    t_red, t_adam = _oracle_time(w, first)
+    n_done = first[0].shape[0]
+    del first
+    per = max(t_red + t_adam, 1e-3)
+    more = min(int(target_s / per), (geom.len - n_done) // chunk)
+    if more > 0:
+        jobs = [(w, geom.offset + n_done + i * chunk, chunk) for i in range(more)]
+        workers = max(1, min(16, len(os.sched_getaffinity(0)) - 1, more))
+        with mp.get_context("fork").Pool(workers) as pool:
+            inputs = pool.map(_oracle_inputs, jobs)
+        for inp in inputs:
+            a, b = _oracle_time(w, inp)
+            t_red, t_adam = t_red + a, t_adam + b
+            n_done += inp[0].shape[0]
+        del inputs
     total = t_red + t_adam
-    return {"value": n / total, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements of the shard: {'' if w.fp16_grad else f'reduce of {w.nd} fp16 rows + '}"
-                      f"one Adam step (NumPy, single thread)",
+    what = "" if w.fp16_grad else f"reduce of {w.nd} fp16 rows + "
+    return {"value": n_done / total, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_done} elements of the shard ({what}one Adam step), NumPy, "
+                      f"one thread, {total:.1f} s of oracle work",
             "reduce_s": t_red, "adam_s": t_adam}
 
 
