@@ -117,6 +117,51 @@ def test_reduce_unaligned(stride_pad, out_shift):
                  stride_pad=stride_pad, out_shift=out_shift)
 
 
+@pytest.mark.parametrize("nd", [2, 15, 31, 33, 48, 63, 65, 97])
+def test_reduce_row_batches(nd):
+    """Nd values whose rows split into every mix of the kernel's load batches
+    (32, then 16, 8, 4, 2, 1): the additions must stay in ascending rank order."""
+    print(f"reduce nd={nd}", flush=True)
+    psi = 40_009 * nd
+    _reduce_case(psi, nd, nd // 2, wl.uniform_buckets(psi, 17_001), wl.Dist(0.05), 2000 + nd)
+
+
+def test_reduce_special_values():
+    """inf, NaN, fp16 subnormals, -0 and sums beyond the fp16 range, against the
+    oracle (NaN compared as NaN, everything else bit for bit)."""
+    nd, n = 5, 4099
+    rng = np.random.default_rng(11)
+    rows = rng.normal(0, 1e-3, size=(nd, n)).astype(np.float16).view(np.uint16)
+    specials = np.array([0x7C00, 0xFC00, 0x7E00, 0x0001, 0x8001, 0x03FF, 0x8000, 0x7BFF,
+                         0xFBFF, 0x0000], np.uint16)
+    for j in range(1000):                      # a special value in some rows of 1000 columns
+        mask = rng.random(nd) < 0.4
+        rows[mask, j] = rng.choice(specials, size=int(mask.sum()))
+    rows[:, 1000] = 0x8000                     # all -0: the mean is +0 (the sum starts at +0)
+    rows[:, 1001] = 0x7BFF                     # sum 5 x 65504 (beyond fp16), mean 65504
+    rows[:, 1002] = [0x7C00, 0xFC00, 0, 0, 0]  # inf + -inf = NaN
+    rows[:, 1003] = 0x0001                     # subnormal sums stay exact
+    geom = Z.shard_geometry(n * nd, nd, 0)       # rank 0 owns flat [0, n)
+    dev_rows = torch.from_numpy(rows.view(np.int16).copy()).cuda()
+    g32 = torch.full((geom.len,), 9.0, device="cuda")
+    g16 = torch.zeros((geom.len,), dtype=torch.int16, device="cuda")
+    Z.reduce_shard(geom, 0, n, dev_rows, g32, g16)
+    torch.cuda.synchronize()
+    w32 = np.full(geom.len, 9.0, np.float32)
+    w16 = np.zeros(geom.len, np.uint16)
+    with np.errstate(all="ignore"):
+        ored.reduce_shard(n * nd, nd, 0, 0, n, rows, w32, w16)
+    got32, got16 = f32(g32), u16(g16)
+    nan32 = np.isnan(got32) & np.isnan(w32)
+    assert np.all((got32.view(np.uint32) == w32.view(np.uint32)) | nan32), "grad32"
+    nan16 = np.isnan(got16.view(np.float16)) & np.isnan(w16.view(np.float16))
+    assert np.all((got16 == w16) | nan16), "grad16"
+    assert got32[1000] == 0 and not np.signbit(got32[1000])
+    assert got32[1001] == 65504.0 and got16[1001] == 0x7BFF
+    assert np.isnan(got32[1002])
+    assert got32[1003] == np.float32(5 * 2.0 ** -24) * np.float32(0.2)
+
+
 def test_reduce_chunking_and_order_invariance():
     psi, nd, rank = 4_000_000, 8, 5
     geom = Z.shard_geometry(psi, nd, rank)
