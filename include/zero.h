@@ -77,6 +77,38 @@ typedef struct zero_geom {
 double zero_memory_model(uint64_t psi, uint32_t nd, int stage);
 
 /*
+ * The same accounting with a general optimizer-state multiplier (guide, "Como
+ * funciona": K Psi bytes of optimizer state, K = 12 for mixed-precision Adam):
+ *   stage 0: (4 + K) Psi          stage 2: 2 Psi + (2 + K) Psi / Nd
+ *   stage 1: 4 Psi + K Psi / Nd   stage 3: (4 + K) Psi / Nd
+ * zero_memory_model(psi, nd, stage) == zero_memory_model_k(psi, nd, stage, 12).
+ * Returns the byte count, or a negative value if nd == 0, the stage is not
+ * 0..3, or k is negative or not finite.
+ */
+double zero_memory_model_k(uint64_t psi, uint32_t nd, int stage, double k);
+
+/* Per-step communication of one data-parallel rank. */
+typedef struct zero_comm {
+  uint32_t reduce_scatters;    /* gradient reduce-scatters per step */
+  uint32_t all_gathers;        /* parameter all-gathers per step */
+  double elems;                /* the guide's count: Psi per collective */
+  double elems_sent_per_rank;  /* bandwidth-optimal collectives: (Nd - 1) / Nd of Psi each */
+  double bytes_sent_per_rank;  /* fp16: 2 bytes per element */
+} zero_comm_t;
+
+/*
+ * Communication volume per step (guide, "Como funciona": plain DP moves 2 Psi,
+ * a reduce-scatter and an all-gather of Psi each; P_os+g keeps 2 Psi; P_os+g+p
+ * needs two parameter all-gathers, in forward and backward, plus the gradient
+ * reduce-scatter, 3 Psi or 1.5x; lastdictionary entry "ZeRO": stages 1 and 2
+ * keep data parallelism's volume).  Fills *out: stages 0-2 one reduce-scatter
+ * and one all-gather, stage 3 one reduce-scatter and two all-gathers.  Pure
+ * host arithmetic.  Errors: ZERO_E_INVAL for out == NULL, nd == 0 or a stage
+ * not 0..3.
+ */
+int zero_comm_volume(uint64_t psi, uint32_t nd, int stage, zero_comm_t *out);
+
+/*
  * Partition of `rank` (card "ZeRO-2", "Why all-gather is still needed": the
  * all-gather of the rank shards in rank order rebuilds [A, B, C]): shard size
  * S = ceil(psi / nd); rank r owns [min(r S, psi), min((r + 1) S, psi)), so

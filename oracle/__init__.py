@@ -10,6 +10,7 @@ torch): the two share only the seeded input generators in ``synth``.
 
 Modules:
   memory_model -- per-device model-state bytes of plain DP and ZeRO stages 1-3
+  comm_model   -- per-step communication volume of plain DP and ZeRO stages 1-3
   geometry     -- contiguous rank-major shards, bucket/shard intersections
   reduce       -- the owner's reduce-scatter slice of one gradient bucket
   adam         -- the sharded mixed-precision Adam step and the fp16 slot write
@@ -18,4 +19,4 @@ Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (printed values, closed forms, brute force, an fp64 textbook
 shadow); see each module's header for the pins.
 """
-from . import adam, geometry, memory_model, reduce  # noqa: F401
+from . import adam, comm_model, geometry, memory_model, reduce  # noqa: F401

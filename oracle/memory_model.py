@@ -14,9 +14,16 @@ fp16 parameters (2 Psi) plus an fp16 gradient shard and the optimizer shard,
 2 Psi + (2 + K) Psi / Nd, the one form that reproduces the guide's worked
 figure of 16.6 GB for 7.5B parameters at Nd = 64 (section "Na pratica").
 
+The guide writes the optimizer state as K Psi with K = 12 for mixed-precision
+Adam; `k` keeps that multiplier general (the stage formulas are the same with
+12 replaced by K: (4 + K) Psi, 4 Psi + K Psi / Nd, 2 Psi + (2 + K) Psi / Nd,
+(4 + K) Psi / Nd).
+
 Pins (tests/test_oracle_memory_model.py): the printed 120 / 31.4 / 16.6 / 1.9 GB
 (tests/golden/memory_model_7p5b_nd64.json), the 16 Psi total, the limits of
-4x and 8x as Nd grows, and 16 Psi / Nd linear in Nd.
+4x and 8x as Nd grows, and 16 Psi / Nd linear in Nd; for general K, the limits
+(4 + K) / 4 and (4 + K) / 2 and a brute-force sum over the bytes each stage
+keeps per parameter.
 """
 from __future__ import annotations
 

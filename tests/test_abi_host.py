@@ -13,6 +13,7 @@ import pytest
 import zero_sharded_mixed_bucketed_amd as Z
 from conftest import ROOT
 from oracle import adam as oadam
+from oracle import comm_model as ocm
 from oracle import geometry as ogeo
 from oracle import memory_model as omm
 
@@ -40,6 +41,34 @@ def test_memory_model_matches_oracle_and_print():
                 assert Z.memory_model(psi, nd, st) == omm.bytes_per_device(psi, nd, st)
     assert [round(Z.memory_model(7_500_000_000, 64, s) / 1e9, 1) for s in range(4)] == \
         [120.0, 31.4, 16.6, 1.9]
+
+
+def test_memory_model_k_matches_oracle():
+    for psi in (1 << 20, 7_500_000_000, 10 ** 11):
+        for nd in (1, 4, 64, 400):
+            for st in range(4):
+                for k in (0.0, 4.0, 12.0, 16.0, 14.5):
+                    assert Z.memory_model_k(psi, nd, st, k) == omm.bytes_per_device(psi, nd, st, k)
+                assert Z.memory_model_k(psi, nd, st, 12.0) == Z.memory_model(psi, nd, st)
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(Z.ZeroError):
+            Z.memory_model_k(100, 4, 0, bad)
+
+
+def test_comm_volume_matches_oracle():
+    for psi in (1, 1 << 20, 7_500_000_000, 10 ** 11):
+        for nd in (1, 2, 3, 64, 400):
+            for st in range(4):
+                c = Z.comm_volume(psi, nd, st)
+                o = ocm.comm_volume(psi, nd, st)
+                assert c.reduce_scatters == o.collectives.count("reduce_scatter")
+                assert c.all_gathers == o.collectives.count("all_gather")
+                assert c.elems == o.elems
+                assert c.elems_sent_per_rank == o.elems_sent_per_rank
+                assert c.bytes_sent_per_rank == o.bytes_sent_per_rank
+    for nd, st in ((0, 0), (4, -1), (4, 4)):
+        with pytest.raises(Z.ZeroError):
+            Z.comm_volume(100, nd, st)
 
 
 def test_memory_model_rejects():

@@ -133,3 +133,70 @@ def test_reduce_shard_offset_mutant_fails(monkeypatch):
     monkeypatch.setattr(red, "reduce_shard", shifted)
     with pytest.raises(AssertionError):
         pins_reduce.test_brute_force_all_ranks(37, 3, 10)
+
+
+# ---- communication and K-general memory model ---------------------------------------
+
+import test_oracle_comm_model as pins_comm  # noqa: E402
+from oracle import comm_model as cm  # noqa: E402
+from oracle import memory_model as mm  # noqa: E402
+
+
+def _comm(mutation):
+    real = cm.comm_volume
+
+    def comm_volume(psi, nd, stage):
+        c = real(psi, nd, stage)
+        if mutation == "stage3_one_all_gather" and stage == 3:
+            return cm.Comm(("all_gather", "reduce_scatter"), 2 * psi, 2 * psi * (nd - 1) / nd)
+        if mutation == "no_ring_factor":
+            return cm.Comm(c.collectives, c.elems, c.elems)
+        if mutation == "stage1_all_reduce_plus_gather" and stage == 1:
+            return cm.Comm(("reduce_scatter", "all_gather", "all_gather"), 3 * psi,
+                           3 * psi * (nd - 1) / nd)
+        return c
+    return comm_volume
+
+
+@pytest.mark.parametrize("mutation", ["stage3_one_all_gather", "no_ring_factor",
+                                      "stage1_all_reduce_plus_gather"])
+def test_comm_mutants_fail_a_pin(monkeypatch, mutation):
+    monkeypatch.setattr(cm, "comm_volume", _comm(mutation))
+    failed = 0
+    checks = [pins_comm.test_pages_counts, pins_comm.test_exact_limits,
+              lambda: [pins_comm.test_exact_per_rank_volume_by_ring_count(nd, st)
+                       for nd in (2, 3) for st in range(4)]]
+    for fn in checks:
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    assert failed, mutation
+
+
+def _mem(mutation):
+    real = mm.bytes_per_device
+
+    def bytes_per_device(psi, nd, stage, k=mm.K_ADAM):
+        if mutation == "k_on_grads_too" and stage == 2:
+            return 2 * psi + (2 * k + k) * psi / nd / 2 + 0.5 * k * psi / nd
+        if mutation == "stage1_grads_sharded" and stage == 1:
+            return 2 * psi + (2 + k) * psi / nd
+        if mutation == "fixed_k" and k != mm.K_ADAM:
+            return real(psi, nd, stage, mm.K_ADAM)
+        return real(psi, nd, stage, k)
+    return bytes_per_device
+
+
+@pytest.mark.parametrize("mutation", ["k_on_grads_too", "stage1_grads_sharded", "fixed_k"])
+def test_memory_k_mutants_fail_a_pin(monkeypatch, mutation):
+    monkeypatch.setattr(mm, "bytes_per_device", _mem(mutation))
+    failed = 0
+    for fn in (lambda: [pins_comm.test_memory_k_brute_force(k, nd, st)
+                        for k in (4, 12) for nd in (2, 4) for st in range(4)],
+               lambda: [pins_comm.test_memory_k_limits(k) for k in (4, 12, 20)]):
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    assert failed, mutation

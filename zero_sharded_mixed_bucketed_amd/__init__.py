@@ -6,6 +6,8 @@ Argument marshalling only: every step runs in the HIP kernels of libzero.so
 names follow the C ABI in ``include/zero.h``:
 
     memory_model(psi, nd, stage)                -> bytes per device
+    memory_model_k(psi, nd, stage, k)           -> the same with K bytes of optimizer state
+    comm_volume(psi, nd, stage)                 -> Comm (collectives and elements per step)
     shard_geometry(psi, nd, rank)               -> Geom
     bucket_intersect(geom, offset, length)      -> (lo, hi)
     reduce_shard(geom, bucket_offset, bucket_len, slices, grad32, grad16=None)
@@ -34,7 +36,8 @@ ZERO_E_DEVICE = -4
 STAGE_DP, STAGE_OS, STAGE_OS_G, STAGE_OS_G_P = 0, 1, 2, 3
 
 # Symbols that include/zero.h declares.
-EXPORTS = ("zero_memory_model", "zero_shard_geometry", "zero_bucket_intersect",
+EXPORTS = ("zero_memory_model", "zero_memory_model_k", "zero_comm_volume",
+           "zero_shard_geometry", "zero_bucket_intersect",
            "zero_reduce_shard", "zero_adam_scalars", "zero_adam_step_shard",
            "zero_last_error")
 
@@ -52,6 +55,12 @@ class Geom(ctypes.Structure):
     def __repr__(self):
         return (f"Geom(psi={self.psi}, nd={self.nd}, rank={self.rank}, offset={self.offset}, "
                 f"len={self.len})")
+
+
+class Comm(ctypes.Structure):
+    _fields_ = [("reduce_scatters", ctypes.c_uint32), ("all_gathers", ctypes.c_uint32),
+                ("elems", ctypes.c_double), ("elems_sent_per_rank", ctypes.c_double),
+                ("bytes_sent_per_rank", ctypes.c_double)]
 
 
 class Shard(ctypes.Structure):
@@ -88,6 +97,10 @@ def _load() -> ctypes.CDLL:
     G = ctypes.POINTER(Geom)
     lib.zero_memory_model.argtypes = [u64, u32, ci]
     lib.zero_memory_model.restype = dbl
+    lib.zero_memory_model_k.argtypes = [u64, u32, ci, dbl]
+    lib.zero_memory_model_k.restype = dbl
+    lib.zero_comm_volume.argtypes = [u64, u32, ci, ctypes.POINTER(Comm)]
+    lib.zero_comm_volume.restype = ci
     lib.zero_shard_geometry.argtypes = [u64, u32, u32, G]
     lib.zero_shard_geometry.restype = ci
     lib.zero_bucket_intersect.argtypes = [G, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(u64)]
@@ -121,6 +134,21 @@ def memory_model(psi: int, nd: int, stage: int) -> float:
     if b < 0:
         raise ZeroError(ZERO_E_INVAL, last_error())
     return b
+
+
+def memory_model_k(psi: int, nd: int, stage: int, k: float) -> float:
+    """Model-state bytes per device with K bytes of optimizer state per parameter."""
+    b = lib.zero_memory_model_k(psi, nd, stage, k)
+    if b < 0:
+        raise ZeroError(ZERO_E_INVAL, last_error())
+    return b
+
+
+def comm_volume(psi: int, nd: int, stage: int) -> Comm:
+    """Per-step communication of one rank for stage 0 (DP), 1, 2 or 3."""
+    c = Comm()
+    _check(lib.zero_comm_volume(psi, nd, stage, ctypes.byref(c)))
+    return c
 
 
 def shard_geometry(psi: int, nd: int, rank: int) -> Geom:

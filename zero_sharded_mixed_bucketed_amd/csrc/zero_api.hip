@@ -118,22 +118,44 @@ void derive_scalars(double lr, double beta1, double beta2, double eps, uint64_t 
 
 extern "C" {
 
-double zero_memory_model(uint64_t psi, uint32_t nd, int stage) {
+double zero_memory_model_k(uint64_t psi, uint32_t nd, int stage, double k) {
   if (nd == 0) {
     fail(ZERO_E_INVAL, "nd must be >= 1");
     return -1.0;
   }
+  if (!(k >= 0.0) || !isfinite(k)) {
+    fail(ZERO_E_INVAL, "k must be finite and >= 0");
+    return -1.0;
+  }
   const double p = static_cast<double>(psi);
   const double n = static_cast<double>(nd);
-  const double params = 2.0 * p, grads = 2.0 * p, optim = 12.0 * p;
-  ok();
+  const double params = 2.0 * p, grads = 2.0 * p, optim = k * p;
   switch (stage) {
-    case ZERO_STAGE_DP: return params + grads + optim;
-    case ZERO_STAGE_OS: return params + grads + optim / n;
-    case ZERO_STAGE_OS_G: return params + (grads + optim) / n;
-    case ZERO_STAGE_OS_G_P: return (params + grads + optim) / n;
+    case ZERO_STAGE_DP: ok(); return params + grads + optim;
+    case ZERO_STAGE_OS: ok(); return params + grads + optim / n;
+    case ZERO_STAGE_OS_G: ok(); return params + (grads + optim) / n;
+    case ZERO_STAGE_OS_G_P: ok(); return (params + grads + optim) / n;
     default: fail(ZERO_E_INVAL, "stage must be 0..3"); return -1.0;
   }
+}
+
+double zero_memory_model(uint64_t psi, uint32_t nd, int stage) {
+  return zero_memory_model_k(psi, nd, stage, 12.0);
+}
+
+int zero_comm_volume(uint64_t psi, uint32_t nd, int stage, zero_comm_t* out) {
+  if (!out) return fail(ZERO_E_INVAL, "out is NULL");
+  if (nd == 0) return fail(ZERO_E_INVAL, "nd must be >= 1");
+  if (stage < ZERO_STAGE_DP || stage > ZERO_STAGE_OS_G_P)
+    return fail(ZERO_E_INVAL, "stage must be 0..3");
+  out->reduce_scatters = 1;
+  out->all_gathers = stage == ZERO_STAGE_OS_G_P ? 2 : 1;
+  const double c = static_cast<double>(out->reduce_scatters + out->all_gathers);
+  const double p = static_cast<double>(psi);
+  out->elems = c * p;
+  out->elems_sent_per_rank = c * p * static_cast<double>(nd - 1) / static_cast<double>(nd);
+  out->bytes_sent_per_rank = 2.0 * out->elems_sent_per_rank;
+  return ok();
 }
 
 int zero_shard_geometry(uint64_t psi, uint32_t nd, uint32_t rank, zero_geom_t* out) {
