@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zero2-7.5B-nd64",
-                    choices=["zero2-7.5B-nd64", "zero2-13B-nd32", "plain-dp-1.4B",
-                             "tiny-zero2"])
+                    choices=["zero2-7.5B-nd64", "zero2-7.5B-nd64-g16", "zero2-13B-nd32",
+                             "plain-dp-1.4B", "tiny-zero2"])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunk", type=int, default=1 << 22,
@@ -56,6 +56,8 @@ def workload(name, rank):
     from synth import workloads as wl
     if name == "zero2-7.5B-nd64":
         return wl.zero2_7p5b(0 if rank is None else rank)
+    if name == "zero2-7.5B-nd64-g16":
+        return wl.zero2_7p5b_g16(0 if rank is None else rank)
     if name == "zero2-13B-nd32":
         return wl.zero2_13b(0 if rank is None else rank)
     if name == "plain-dp-1.4B":
@@ -100,7 +102,8 @@ def main():
             sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
                                 kind=gen.KIND_GRAD_FULL)
         else:
-            grad = torch.zeros(S, dtype=torch.float32, device=dev)
+            g16 = w.grad_shard == "fp16"
+            grad = torch.zeros(S, dtype=torch.int16 if g16 else torch.float32, device=dev)
             for off, n in wl.buckets_touching(w.buckets, lo, lo + S):
                 a, b = Z.bucket_intersect(geom, off, n)
                 stride = (b - a + 63) // 64 * 64     # rows start on 128-byte cache lines
@@ -135,7 +138,10 @@ def main():
         for i, (a, n, rows) in enumerate(buckets):
             if events is not None:
                 events["reduce"][i][0].record(stream)
-            Z.reduce_shard(geom, a, n, rows, grad, stream=stream)
+            if grad.dtype == torch.float32:
+                Z.reduce_shard(geom, a, n, rows, grad, stream=stream)
+            else:
+                Z.reduce_shard(geom, a, n, rows, None, grad, stream=stream)
             if events is not None:
                 events["reduce"][i][1].record(stream)
         if events is not None:
@@ -169,8 +175,9 @@ def main():
 
     # algorithmic bytes: reduce reads 2 Nd and writes 4 bytes per owned element;
     # Adam reads g, master, m, v and writes master, m, v and the fp16 slot.
-    red_bytes = S * (2 * w.nd + 4) if buckets else 0
-    adam_bytes = S * (28 if w.fp16_grad else 30)
+    g_bytes = 4 if grad.dtype == torch.float32 else 2     # gradient shard element
+    red_bytes = S * (2 * w.nd + g_bytes) if buckets else 0
+    adam_bytes = S * (26 + g_bytes)
     ms_step = total_ms / args.steps
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
     red_avg = sum(red_ms) / args.steps
@@ -187,7 +194,7 @@ def main():
         kernels["reduce"] = {
             "kernel": "reduce_kernel", "launches_per_step": len(buckets),
             "avg_ms_per_launch": sum(red_ms) / n_red_launch, "avg_ms_per_step": red_avg,
-            "bytes_per_step": red_bytes, "bytes_per_element": 2 * w.nd + 4,
+            "bytes_per_step": red_bytes, "bytes_per_element": 2 * w.nd + g_bytes,
             "gbs": gbs(red_bytes, red_avg), "frac_of_peak": gbs(red_bytes, red_avg) / PEAK_HBM_GBS,
             "params_per_s": S / (red_avg * 1e-3)}
     dom = max(kernels, key=lambda k: kernels[k].get("avg_ms_per_step", kernels[k].get("avg_ms")))
@@ -227,6 +234,7 @@ def main():
         "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
                    "shard_elements": S, "buckets_in_shard": len(buckets),
                    "bucket_elements": wl.BUCKET, "grad": "fp16 rows" if buckets else "fp16",
+                   "grad_shard": ("fp32" if g_bytes == 4 else "fp16") if buckets else None,
                    "state": "fp32 master/m/v", "slot": "fp16"},
         "kernels": kernels,
         "roofline": roofline,
@@ -280,8 +288,13 @@ def self_check(w, geom, buckets, grad, master, m, v, param16, idx, steps_done):
         rows = np.stack([gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
                          for k in range(w.nd)])
         g_ref = ored.reduce_values(rows, w.nd)
-        g_dev = grad.index_select(0, it).cpu().numpy()
-        reduce_ok = bool(np.array_equal(g_ref.view(np.uint32), g_dev.view(np.uint32)))
+        if grad.dtype == torch.float32:
+            g_dev = grad.index_select(0, it).cpu().numpy()
+            reduce_ok = bool(np.array_equal(g_ref.view(np.uint32), g_dev.view(np.uint32)))
+        else:
+            g_ref = g_ref.astype(np.float16).view(np.uint16)      # the fp16 gradient shard
+            g_dev = grad.index_select(0, it).cpu().numpy().view(np.uint16)
+            reduce_ok = bool(np.array_equal(g_ref, g_dev))
     else:
         g_ref = gen.grad_f16(w.seed, 0, flat, w.grad.sigma, w.grad.heavy_tail,
                              kind=gen.KIND_GRAD_FULL)
@@ -328,6 +341,8 @@ def _oracle_time(w, inputs):
     t0 = time.perf_counter()
     if not w.fp16_grad:
         g = ored.reduce_values(g, w.nd)
+        if w.grad_shard == "fp16":
+            g = g.astype(np.float16).view(np.uint16)
     t1 = time.perf_counter()
     oadam.step_values(th, mm, vv, g, oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, 1))
     t2 = time.perf_counter()

@@ -137,18 +137,28 @@ int zero_bucket_intersect(const zero_geom_t *g, uint64_t bucket_offset, uint64_t
  *   of one.  Only the columns inside the rank's shard are read.  The buffer must
  *   hold (Nd - 1) * slice_stride + bucket_len elements; slice_stride >=
  *   bucket_len.
- * grad32: device, fp32, the rank's shard-local gradient (g->len elements);
- *   for every flat i in bucket-intersect-shard,
+ * grad32: device, fp32, the rank's shard-local gradient (g->len elements), or
+ *   NULL to keep only the fp16 gradient shard; for every flat i in
+ *   bucket-intersect-shard,
  *     grad32[i - g->offset] = RN32(sum_{k = 0..Nd-1} fp32(row_k[i])) * RN32(1/Nd)
  *   with the additions done one at a time in ascending rank order from +0 (each
  *   rounded to fp32) and one fp32 multiply by the correctly rounded 1/Nd.
  *   Elements outside the intersection are not touched.
  * grad16: optional (NULL = none), device, fp16 bit patterns, g->len elements:
- *   the round-to-nearest-even fp16 of grad32 at the same elements.
+ *   the round-to-nearest-even fp16 of the fp32 value above, at the same
+ *   elements.  This 2-byte gradient shard is the one the guide's stage-2
+ *   accounting keeps (2 Psi + 14 Psi / Nd).  At least one of grad32 and grad16
+ *   must be given.
+ * Aliasing: an output may share memory with the rows only column for column,
+ *   i.e. the output element of flat index i at the address of some row's
+ *   element i.  This is how stage 1 (P_os) keeps its reduced shard inside its
+ *   own retained full local gradient: grad16 = own_local_grad + g->offset where
+ *   row `rank` is own_local_grad + bucket_offset.  Any other overlap is
+ *   undefined.
  * The "release" of the rest of the local gradient is the caller freeing
  * `slices` after this call completes on the stream.  An empty intersection is
  * ZERO_OK and enqueues nothing.
- * Errors: ZERO_E_INVAL (null pointer where data is needed, bad geometry),
+ * Errors: ZERO_E_INVAL (slices NULL, both outputs NULL, bad geometry),
  * ZERO_E_RANGE (bucket beyond psi, slice_stride < bucket_len, size overflow),
  * ZERO_E_ALIGN (slices or grad16 not 2-byte, grad32 not 4-byte aligned),
  * ZERO_E_DEVICE (launch failed).

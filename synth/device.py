@@ -49,7 +49,7 @@ def _table(key, maker, dtype, device):
     k = (key, dtype, str(device))
     if k not in _tables:
         host = maker()
-        _tables[k] = torch.from_numpy(np.ascontiguousarray(host).view(
+        _tables[k] = torch.from_numpy(np.array(host, copy=True).view(
             np.int16 if dtype == torch.int16 else np.float32)).to(device)
     return _tables[k]
 

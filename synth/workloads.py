@@ -48,6 +48,9 @@ class Workload:
     # Nd = 1 plain data parallelism: the optimizer reads the raw fp16 gradient
     # (no reduce, no fp32 gradient shard).
     fp16_grad: bool = False
+    # ZeRO-2 gradient shard the reduce writes and Adam reads: "fp32", or "fp16"
+    # (the 2-byte gradient shard of the guide's 2 Psi + 14 Psi / Nd accounting).
+    grad_shard: str = "fp32"
     extra: dict = field(default_factory=dict, compare=False)
 
 
@@ -122,6 +125,13 @@ def zero2_7p5b(rank: int = 0) -> Workload:
         buckets=uniform_buckets(psi), grad=Dist(1e-3), master=Dist(0.02),
         m=Dist(1e-4), v=Dist(1e-6, absolute=True), lr=1e-4, steps=10,
         seed=_c(2))
+
+
+def zero2_7p5b_g16(rank: int = 0) -> Workload:
+    """The 7.5B / Nd = 64 rank with an fp16 gradient shard."""
+    w = zero2_7p5b(rank)
+    return Workload(**{**w.__dict__, "name": f"zero2-7.5B-nd64-g16-r{rank}",
+                       "grad_shard": "fp16"})
 
 
 def zero2_13b(rank: int = 0) -> Workload:

@@ -147,7 +147,8 @@ def _reduce(g, off=25, n=25, slices=FAKE, stride=25, g32=FAKE, g16=None):
     (lambda: _reduce(_geom(), off=90, n=20), Z.ZERO_E_RANGE),      # beyond psi
     (lambda: _reduce(_geom(), off=2 ** 64 - 5, n=10), Z.ZERO_E_RANGE),
     (lambda: _reduce(_geom(), slices=None), Z.ZERO_E_INVAL),
-    (lambda: _reduce(_geom(), g32=None), Z.ZERO_E_INVAL),
+    (lambda: _reduce(_geom(), g32=None), Z.ZERO_E_INVAL),         # no output at all
+    (lambda: _reduce(_geom(), g32=None, g16=FAKE + 1), Z.ZERO_E_ALIGN),
     (lambda: _reduce(_geom(), stride=24), Z.ZERO_E_RANGE),
     (lambda: _reduce(_geom(), stride=2 ** 63), Z.ZERO_E_RANGE),    # size overflow
     (lambda: _reduce(_geom(), slices=FAKE + 1), Z.ZERO_E_ALIGN),

@@ -189,11 +189,12 @@ def _dev(t, name, dtypes, numel_at_least=None):
 
 def reduce_shard(geom: Geom, bucket_offset: int, bucket_len: int, slices, grad32,
                  grad16=None, stream=None) -> None:
-    """The owner's reduce of one bucket (or chunk) into grad32 (and grad16).
+    """The owner's reduce of one bucket (or chunk) into grad32 and/or grad16.
 
     slices: int16/float16 device tensor [Nd, >= bucket_len] (row stride =
     slices.stride(0)); row k is rank k's local gradient over the bucket.
-    grad32: float32 [geom.len]; grad16: optional int16/float16 [geom.len].
+    grad32: float32 [geom.len] or None; grad16: int16/float16 [geom.len] or
+    None (not both None).  An output may alias a row column for column.
     """
     import torch
     f16 = (torch.int16, torch.float16)
@@ -201,15 +202,19 @@ def reduce_shard(geom: Geom, bucket_offset: int, bucket_len: int, slices, grad32
     if slices.dim() != 2 or slices.shape[0] != geom.nd or slices.stride(1) != 1 \
             or slices.shape[1] < bucket_len:
         raise ValueError("slices must be [Nd, >= bucket_len] with unit column stride")
-    _dev(grad32, "grad32", (torch.float32,), geom.len)
-    if not grad32.is_contiguous():
-        raise ValueError("grad32 must be contiguous")
+    if grad32 is None and grad16 is None:
+        raise ValueError("grad32 and grad16 are both None")
+    if grad32 is not None:
+        _dev(grad32, "grad32", (torch.float32,), geom.len)
+        if not grad32.is_contiguous():
+            raise ValueError("grad32 must be contiguous")
     if grad16 is not None:
         _dev(grad16, "grad16", f16, geom.len)
         if not grad16.is_contiguous():
             raise ValueError("grad16 must be contiguous")
     _check(lib.zero_reduce_shard(ctypes.byref(geom), bucket_offset, bucket_len,
-                                 slices.data_ptr(), slices.stride(0), grad32.data_ptr(),
+                                 slices.data_ptr(), slices.stride(0),
+                                 grad32.data_ptr() if grad32 is not None else None,
                                  grad16.data_ptr() if grad16 is not None else None,
                                  _stream_handle(stream)))
 

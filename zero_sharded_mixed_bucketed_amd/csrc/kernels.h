@@ -15,7 +15,7 @@ struct ReduceLaunch {
   uint32_t nd;
   uint64_t c_lo, c_hi;
   int64_t delta;
-  float* out32;
+  float* out32;     // nullable (not both)
   uint16_t* out16;  // nullable
   float inv_nd;
 };

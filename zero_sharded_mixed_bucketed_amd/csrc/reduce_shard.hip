@@ -14,7 +14,10 @@
 // the last full batch go in batches of 16, 8, 4, 2 and 1.  A workgroup is one
 // wavefront and reads 1 KiB contiguous per row.  Vectorisation is across
 // elements, never across ranks, so each element's additions keep the rank
-// order and the result is bit-exact.
+// order and the result is bit-exact.  A thread reads every row of its
+// columns before it writes their outputs, and no other thread touches those
+// columns, so an output may share memory with a row column for column (the
+// reduced value replacing that row's element in place).
 //
 // On MI355X a pure 64-row read of this shape streams at about 7.2 TB/s; the
 // 4 bytes per element written back cost the rest (writes that leave L2 while
@@ -75,17 +78,19 @@ struct Args {
 };
 
 __device__ __forceinline__ void store_full(const Args& a, uint64_t o, const float (&r)[kCols]) {
-  float* p = a.out32 + o;
-  if (a.st32 == 4) {
-    __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(f32x4{r[4], r[5], r[6], r[7]}, reinterpret_cast<f32x4*>(p + 4));
-  } else if (a.st32 == 2) {
+  if (a.out32) {
+    float* p = a.out32 + o;
+    if (a.st32 == 4) {
+      __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, reinterpret_cast<f32x4*>(p));
+      __builtin_nontemporal_store(f32x4{r[4], r[5], r[6], r[7]}, reinterpret_cast<f32x4*>(p + 4));
+    } else if (a.st32 == 2) {
 #pragma unroll
-    for (int e = 0; e < kCols; e += 2)
-      __builtin_nontemporal_store(f32x2{r[e], r[e + 1]}, reinterpret_cast<f32x2*>(p + e));
-  } else {
+      for (int e = 0; e < kCols; e += 2)
+        __builtin_nontemporal_store(f32x2{r[e], r[e + 1]}, reinterpret_cast<f32x2*>(p + e));
+    } else {
 #pragma unroll
-    for (int e = 0; e < kCols; ++e) __builtin_nontemporal_store(r[e], p + e);
+      for (int e = 0; e < kCols; ++e) __builtin_nontemporal_store(r[e], p + e);
+    }
   }
   if (a.out16) {
     uint16_t* q = a.out16 + o;
@@ -93,15 +98,18 @@ __device__ __forceinline__ void store_full(const Args& a, uint64_t o, const floa
 #pragma unroll
     for (int e = 0; e < kCols; ++e) h[e] = f2h(r[e]);
     if (a.st16 == 8) {
-      *reinterpret_cast<u32x4*>(q) =
-          u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      __builtin_nontemporal_store(
+          u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
+          reinterpret_cast<u32x4*>(q));
     } else if (a.st16 == 4) {
-      *reinterpret_cast<u32x2*>(q) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(q + 4) = u32x2{h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      __builtin_nontemporal_store(u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)},
+                                  reinterpret_cast<u32x2*>(q));
+      __builtin_nontemporal_store(u32x2{h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
+                                  reinterpret_cast<u32x2*>(q + 4));
     } else if (a.st16 == 2) {
 #pragma unroll
       for (int e = 0; e < kCols; e += 2)
-        *reinterpret_cast<uint32_t*>(q + e) = h[e] | (h[e + 1] << 16);
+        __builtin_nontemporal_store(h[e] | (h[e + 1] << 16), reinterpret_cast<uint32_t*>(q + e));
     } else {
 #pragma unroll
       for (int e = 0; e < kCols; ++e) q[e] = static_cast<uint16_t>(h[e]);
@@ -186,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
     if (col >= a.c_lo && col < a.c_hi) {
       const float r = acc[e] * a.inv;
       const uint64_t o = static_cast<uint64_t>(static_cast<int64_t>(col) + a.delta);
-      a.out32[o] = r;
+      if (a.out32) a.out32[o] = r;
       if (a.out16) a.out16[o] = static_cast<uint16_t>(f2h(r));
     }
   }
@@ -214,8 +222,11 @@ hipError_t launch_reduce(const ReduceLaunch& L, int /*cus*/, hipStream_t stream)
   // Alignment of the output addresses of full groups: column col0 + 8j maps to
   // out32 + col0 + delta + 8j, so the alignment class is the same for all.
   const uint64_t o0 = static_cast<uint64_t>(static_cast<int64_t>(a.col0) + a.delta);
-  const uintptr_t b32 = reinterpret_cast<uintptr_t>(L.out32) + 4 * o0;
-  a.st32 = (b32 % 16 == 0) ? 4 : (b32 % 8 == 0) ? 2 : 1;
+  a.st32 = 1;
+  if (L.out32) {
+    const uintptr_t b32 = reinterpret_cast<uintptr_t>(L.out32) + 4 * o0;
+    a.st32 = (b32 % 16 == 0) ? 4 : (b32 % 8 == 0) ? 2 : 1;
+  }
   a.st16 = 1;
   if (L.out16) {
     const uintptr_t b16 = reinterpret_cast<uintptr_t>(L.out16) + 2 * o0;

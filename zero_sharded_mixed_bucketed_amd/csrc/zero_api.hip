@@ -191,13 +191,14 @@ int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t buc
   const uint64_t a = bucket_offset > s_lo ? bucket_offset : s_lo;
   const uint64_t b = (bucket_offset + bucket_len) < s_hi ? (bucket_offset + bucket_len) : s_hi;
   if (a >= b) return ok();  // nothing of this bucket is owned here
-  if (!slices || !grad32) return fail(ZERO_E_INVAL, "slices and grad32 must not be NULL");
+  if (!slices) return fail(ZERO_E_INVAL, "slices must not be NULL");
+  if (!grad32 && !grad16) return fail(ZERO_E_INVAL, "grad32 and grad16 are both NULL");
   if (slice_stride < bucket_len)
     return fail(ZERO_E_RANGE, "slice_stride %llu < bucket_len %llu",
                 (unsigned long long)slice_stride, (unsigned long long)bucket_len);
   if (g->nd > 1 && slice_stride > (UINT64_MAX / 2 - bucket_len) / (g->nd - 1))
     return fail(ZERO_E_RANGE, "slice buffer size overflows");
-  if (!aligned(slices, 2) || !aligned(grad32, 4) || (grad16 && !aligned(grad16, 2)))
+  if (!aligned(slices, 2) || (grad32 && !aligned(grad32, 4)) || (grad16 && !aligned(grad16, 2)))
     return fail(ZERO_E_ALIGN, "slices/grad16 need 2-byte and grad32 4-byte alignment");
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
