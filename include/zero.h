@@ -16,7 +16,9 @@
  * This library is the one-GPU share of that path: zero_reduce_shard is the
  * owner's side of one bucket's reduce-scatter, with the Nd ranks' local
  * gradients handed over as Nd rows of one device buffer; zero_adam_step_shard is
- * the fused sharded Adam step and the fp16 slot write.  No collective runs here.
+ * the fused sharded Adam step and the fp16 slot write.  For stage 3, where the
+ * parameters are partitioned too, zero_gather_params is the receive side of a
+ * layer's parameter all-gather.  No collective runs here.
  *
  * Conventions for every entry point:
  *  - Sizes and offsets are element counts (uint64_t).  Flat indices address
@@ -216,6 +218,28 @@ int zero_adam_scalars(double lr, double beta1, double beta2, double eps, uint64_
  */
 int zero_adam_step_shard(const zero_geom_t *g, const zero_shard_t *s, double lr, double beta1,
                          double beta2, double eps, uint64_t step, void *hip_stream);
+
+/*
+ * The receive side of one layer's parameter all-gather in stage 3, P_os+g+p
+ * (guide, "Como funciona": the parameters are partitioned too and a process
+ * that needs another's partition receives it, two parameter all-gathers per
+ * step; lastdictionary entry "ZeRO": each layer's parameters are gathered just
+ * in time and discarded after use; card "ZeRO-2", "Why all-gather is still
+ * needed": the partitions in rank order are the full vector).
+ *
+ * shards: device, fp16 bit patterns, Nd rows; row k (at shards + k *
+ *   shard_stride) is rank k's parameter shard, flat [k S, min((k + 1) S, psi))
+ *   with S = ceil(psi / nd) as in zero_shard_geometry; shard_stride >= S.
+ * out: device, fp16, len elements: out[j] = the parameter of flat index lo + j.
+ *   It must not overlap the shards.
+ * Pure data movement (bit-exact).  len == 0 is ZERO_OK and enqueues nothing.
+ * Errors: ZERO_E_INVAL (nd == 0, psi == 0, NULL buffer), ZERO_E_RANGE (range
+ * beyond psi, shard_stride < S, size overflow), ZERO_E_ALIGN (a buffer not
+ * 2-byte aligned), ZERO_E_DEVICE (launch failed).
+ */
+int zero_gather_params(uint64_t psi, uint32_t nd, uint64_t lo, uint64_t len,
+                       const uint16_t *shards, uint64_t shard_stride, uint16_t *out,
+                       void *hip_stream);
 
 /* Message of the calling thread's last error ("" if none).  Valid until the
  * thread's next call into the library. */

@@ -14,9 +14,10 @@ Modules:
   geometry     -- contiguous rank-major shards, bucket/shard intersections
   reduce       -- the owner's reduce-scatter slice of one gradient bucket
   adam         -- the sharded mixed-precision Adam step and the fp16 slot write
+  stage3       -- the receive side of a stage-3 layer parameter gather
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (printed values, closed forms, brute force, an fp64 textbook
 shadow); see each module's header for the pins.
 """
-from . import adam, comm_model, geometry, memory_model, reduce  # noqa: F401
+from . import adam, comm_model, geometry, memory_model, reduce, stage3  # noqa: F401

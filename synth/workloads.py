@@ -84,6 +84,12 @@ def transformer_tensors(psi: int, hidden: int) -> List[Tuple[int, int]]:
     return out
 
 
+def transformer_layers(psi: int, hidden: int) -> List[Tuple[int, int]]:
+    """Flat (offset, length) of each layer (its three tensors together), forward order."""
+    per = 12 * hidden * hidden + 2 * hidden
+    return [(off, min(per, psi - off)) for off in range(0, psi, per)]
+
+
 def tensor_buckets(psi: int, hidden: int, size: int = BUCKET) -> Tuple[Tuple[int, int], ...]:
     """Buckets = tensors in reverse order, each cut from its end into <= size pieces."""
     out: List[Tuple[int, int]] = []

@@ -212,3 +212,29 @@ def test_one_hip_runtime_in_process():
     from synth import device as sdev
     sdev._load()
     assert len(Z.hip_runtimes()) == 1, Z.hip_runtimes()
+
+
+def _gather(psi=100, nd=4, lo=10, n=20, shards=FAKE, stride=25, out=FAKE):
+    return Z.lib.zero_gather_params(psi, nd, lo, n, shards, stride, out, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _gather(nd=0), Z.ZERO_E_INVAL),
+    (lambda: _gather(psi=0), Z.ZERO_E_INVAL),
+    (lambda: _gather(lo=90, n=11), Z.ZERO_E_RANGE),                # beyond psi
+    (lambda: _gather(lo=2 ** 64 - 5, n=10), Z.ZERO_E_RANGE),
+    (lambda: _gather(shards=None), Z.ZERO_E_INVAL),
+    (lambda: _gather(out=None), Z.ZERO_E_INVAL),
+    (lambda: _gather(stride=24), Z.ZERO_E_RANGE),                  # stride < S = 25
+    (lambda: _gather(stride=2 ** 63), Z.ZERO_E_RANGE),             # size overflow
+    (lambda: _gather(shards=FAKE + 1), Z.ZERO_E_ALIGN),
+    (lambda: _gather(out=FAKE + 1), Z.ZERO_E_ALIGN),
+])
+def test_gather_rejects(call, code):
+    assert call() == code
+    assert Z.last_error()
+
+
+def test_gather_empty_is_ok_without_device():
+    assert _gather(n=0, shards=None, out=None) == Z.ZERO_OK
+    assert _gather(lo=100, n=0) == Z.ZERO_OK

@@ -14,6 +14,7 @@ names follow the C ABI in ``include/zero.h``:
     adam_scalars(lr, beta1, beta2, eps, step)   -> 7 fp32 scalars
     adam_step_shard(geom, master, m, v, grad, param16, param16_origin,
                     lr, beta1, beta2, eps, step)
+    gather_params(psi, nd, lo, length, shards, out)
 
 Importing this package fails if libzero.so has not been built: there is no
 fallback path.
@@ -39,7 +40,7 @@ STAGE_DP, STAGE_OS, STAGE_OS_G, STAGE_OS_G_P = 0, 1, 2, 3
 EXPORTS = ("zero_memory_model", "zero_memory_model_k", "zero_comm_volume",
            "zero_shard_geometry", "zero_bucket_intersect",
            "zero_reduce_shard", "zero_adam_scalars", "zero_adam_step_shard",
-           "zero_last_error")
+           "zero_gather_params", "zero_last_error")
 
 
 class ZeroError(RuntimeError):
@@ -111,6 +112,8 @@ def _load() -> ctypes.CDLL:
     lib.zero_adam_scalars.restype = ci
     lib.zero_adam_step_shard.argtypes = [G, ctypes.POINTER(Shard), dbl, dbl, dbl, dbl, u64, vp]
     lib.zero_adam_step_shard.restype = ci
+    lib.zero_gather_params.argtypes = [u64, u32, u64, u64, vp, u64, vp, vp]
+    lib.zero_gather_params.restype = ci
     lib.zero_last_error.argtypes = []
     lib.zero_last_error.restype = ctypes.c_char_p
     return lib
@@ -249,3 +252,21 @@ def adam_step_shard(geom: Geom, master, m, v, grad, param16: Optional[object],
         s.param16_len = param16.numel()
     _check(lib.zero_adam_step_shard(ctypes.byref(geom), ctypes.byref(s), lr, beta1, beta2, eps,
                                     step, _stream_handle(stream)))
+
+
+def gather_params(psi: int, nd: int, lo: int, length: int, shards, out, stream=None) -> None:
+    """Stage 3: the fp16 parameters of flat [lo, lo + length) into out, from the
+    rank shards (int16/float16 device tensor [Nd, >= S], row k = rank k's
+    shard, unit column stride)."""
+    import torch
+    f16 = (torch.int16, torch.float16)
+    _dev(shards, "shards", f16)
+    s = -(-psi // nd) if nd > 0 else 0
+    if shards.dim() != 2 or shards.shape[0] != nd or shards.stride(1) != 1 \
+            or shards.shape[1] < s:
+        raise ValueError("shards must be [Nd, >= S] with unit column stride")
+    _dev(out, "out", f16, length)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _check(lib.zero_gather_params(psi, nd, lo, length, shards.data_ptr(), shards.stride(0),
+                                  out.data_ptr(), _stream_handle(stream)))

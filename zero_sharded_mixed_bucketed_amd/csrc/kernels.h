@@ -33,10 +33,25 @@ struct AdamLaunch {
   float b1, b2, c1, c2, eps, step, isb;
 };
 
-// Both return hipSuccess or the launch error.  `cus` is the device's compute
+// The parameters of flat [lo, lo + n) gathered from the rank shards: row k at
+// shards + k * stride holds flat [k * s, (k + 1) * s).
+struct GatherLaunch {
+  const uint16_t* shards;
+  uint64_t stride;
+  uint64_t s;
+  uint64_t lo, n;
+  uint16_t* out;
+};
+
+// A gather crossing more rank shards than this runs as one element-wise launch
+// instead of one copy per shard piece.
+constexpr uint64_t kMaxGatherPieces = 16;
+
+// All return hipSuccess or the launch error.  `cus` is the device's compute
 // unit count, used to size grid-stride launches.
 hipError_t launch_reduce(const ReduceLaunch& a, int cus, hipStream_t stream);
 hipError_t launch_adam(const AdamLaunch& a, int cus, hipStream_t stream);
+hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 
 }  // namespace zero
 

@@ -272,6 +272,35 @@ int zero_adam_step_shard(const zero_geom_t* g, const zero_shard_t* s, double lr,
   return ok();
 }
 
+int zero_gather_params(uint64_t psi, uint32_t nd, uint64_t lo, uint64_t len,
+                       const uint16_t* shards, uint64_t shard_stride, uint16_t* out,
+                       void* hip_stream) {
+  if (nd == 0 || psi == 0) return fail(ZERO_E_INVAL, "need psi > 0 and nd > 0");
+  if (lo > psi || len > psi - lo)
+    return fail(ZERO_E_RANGE, "range [%llu, +%llu) leaves the parameter vector (psi=%llu)",
+                (unsigned long long)lo, (unsigned long long)len, (unsigned long long)psi);
+  if (len == 0) return ok();
+  if (!shards || !out) return fail(ZERO_E_INVAL, "shards and out must not be NULL");
+  const uint64_t s = psi / nd + (psi % nd != 0);
+  if (shard_stride < s)
+    return fail(ZERO_E_RANGE, "shard_stride %llu < shard size %llu",
+                (unsigned long long)shard_stride, (unsigned long long)s);
+  if (nd > 1 && shard_stride > (UINT64_MAX / 2 - s) / (nd - 1))
+    return fail(ZERO_E_RANGE, "shard buffer size overflows");
+  if (!aligned(shards, 2) || !aligned(out, 2))
+    return fail(ZERO_E_ALIGN, "shards and out need 2-byte alignment");
+  zero::GatherLaunch L;
+  L.shards = shards;
+  L.stride = shard_stride;
+  L.s = s;
+  L.lo = lo;
+  L.n = len;
+  L.out = out;
+  hipError_t e = zero::launch_gather(L, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(ZERO_E_DEVICE, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* zero_last_error(void) { return g_err; }
 
 }  // extern "C"
