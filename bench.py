@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zero2-7.5B-nd64",
-                    choices=["zero2-7.5B-nd64", "zero2-7.5B-nd64-g16", "zero2-13B-nd32",
-                             "plain-dp-1.4B", "tiny-zero2"])
+                    choices=["zero2-7.5B-nd64", "zero2-7.5B-nd64-g16", "zero3-7.5B-nd64",
+                             "zero2-13B-nd32", "plain-dp-1.4B", "tiny-zero2"])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunk", type=int, default=1 << 22,
@@ -58,6 +58,8 @@ def workload(name, rank):
         return wl.zero2_7p5b(0 if rank is None else rank)
     if name == "zero2-7.5B-nd64-g16":
         return wl.zero2_7p5b_g16(0 if rank is None else rank)
+    if name == "zero3-7.5B-nd64":
+        return wl.zero3_7p5b(0 if rank is None else rank)
     if name == "zero2-13B-nd32":
         return wl.zero2_13b(0 if rank is None else rank)
     if name == "plain-dp-1.4B":
@@ -80,6 +82,7 @@ def main():
     from synth import workloads as wl
 
     w = workload(args.workload, args.rank)
+    stage3 = w.extra.get("stage") == 3
     geom = Z.shard_geometry(w.psi, w.nd, w.rank)
     S, lo = geom.len, geom.offset
     dev = torch.device("cuda", 0)
@@ -88,6 +91,7 @@ def main():
           f"+{S})", file=sys.stderr, flush=True)
 
     # ---- inputs resident in HBM (untimed) ----------------------------------------------
+    shards = layer_buf = None
     with torch.cuda.stream(stream):
         master = torch.empty(S, dtype=torch.float32, device=dev)
         m = torch.empty_like(master)
@@ -95,7 +99,21 @@ def main():
         sdev.fill_state(master, w.seed, gen.KIND_MASTER, lo, w.master.sigma)
         sdev.fill_state(m, w.seed, gen.KIND_M, lo, w.m.sigma, w.m.absolute)
         sdev.fill_state(v, w.seed, gen.KIND_V, lo, w.v.sigma, w.v.absolute)
-        param16 = torch.zeros(w.psi, dtype=torch.int16, device=dev)   # the flat fp16 vector
+        if stage3:
+            # every rank's fp16 parameter shard (the all-gather sources); row
+            # `rank` is this rank's own shard, which its Adam step writes
+            s_all = -(-w.psi // w.nd)
+            shards = torch.empty((w.nd, s_all), dtype=torch.int16, device=dev)
+            for k in range(w.nd):
+                k_lo = min(k * s_all, w.psi)
+                k_n = min((k + 1) * s_all, w.psi) - k_lo
+                if k_n:
+                    sdev.fill_grad_rows(shards[k:k + 1, :k_n], w.seed, k_lo,
+                                        w.extra["param_sigma"], rank0=k, kind=gen.KIND_PARAM16)
+            param16, param16_origin = shards[w.rank, :S], lo
+            layer_buf = torch.empty(max(n for _, n in w.buckets), dtype=torch.int16, device=dev)
+        else:
+            param16, param16_origin = torch.zeros(w.psi, dtype=torch.int16, device=dev), 0
         buckets = []          # (flat offset, length, rows) for the buckets meeting the shard
         if w.fp16_grad:
             grad = torch.empty(S, dtype=torch.int16, device=dev)
@@ -130,26 +148,54 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- one step of the path ------------------------------------------------------------
+    # ---- one step of the path: a list of launches -----------------------------------------
+    # Algorithmic bytes per launch: the reduce reads 2 Nd and writes the gradient
+    # element (4 or 2 bytes) per owned column; Adam reads g, master, m, v and
+    # writes master, m, v and the fp16 parameter (26 bytes + the gradient); a
+    # parameter gather reads and writes 2 bytes per element.
+    g_bytes = 4 if grad.dtype == torch.float32 else 2
+    red_of = {a: rows for a, _, rows in buckets}
+
+    def launches(t):
+        ops = []
+
+        def reduce_op(a, n, rows):
+            if grad.dtype == torch.float32:
+                return lambda: Z.reduce_shard(geom, a, n, rows, grad, stream=stream)
+            return lambda: Z.reduce_shard(geom, a, n, rows, None, grad, stream=stream)
+
+        if stage3:
+            layers = list(reversed(w.buckets))                   # forward order
+            for off, n in layers:                                # forward gathers
+                ops.append(("gather", n * 4, lambda off=off, n=n: Z.gather_params(
+                    w.psi, w.nd, off, n, shards, layer_buf[:n], stream=stream)))
+            for off, n in w.buckets:                             # backward, reverse order
+                ops.append(("gather", n * 4, lambda off=off, n=n: Z.gather_params(
+                    w.psi, w.nd, off, n, shards, layer_buf[:n], stream=stream)))
+                a, b = Z.bucket_intersect(geom, off, n)
+                if a < b:
+                    ops.append(("reduce", (b - a) * (2 * w.nd + g_bytes),
+                                reduce_op(a, b - a, red_of[a])))
+        else:
+            for a, n, rows in buckets:
+                ops.append(("reduce", n * (2 * w.nd + g_bytes), reduce_op(a, n, rows)))
+        ops.append(("adam", S * (26 + g_bytes), lambda: Z.adam_step_shard(
+            geom, master, m, v, grad, param16, param16_origin, w.lr, w.beta1, w.beta2, w.eps,
+            t, stream=stream)))
+        return ops
+
     t_counter = [0]
 
     def step(events=None):
         t_counter[0] += 1
-        for i, (a, n, rows) in enumerate(buckets):
+        ops = launches(t_counter[0])
+        for i, (_, _, fn) in enumerate(ops):
             if events is not None:
-                events["reduce"][i][0].record(stream)
-            if grad.dtype == torch.float32:
-                Z.reduce_shard(geom, a, n, rows, grad, stream=stream)
-            else:
-                Z.reduce_shard(geom, a, n, rows, None, grad, stream=stream)
+                events[i][0].record(stream)
+            fn()
             if events is not None:
-                events["reduce"][i][1].record(stream)
-        if events is not None:
-            events["adam"][0].record(stream)
-        Z.adam_step_shard(geom, master, m, v, grad, param16, 0, w.lr, w.beta1, w.beta2, w.eps,
-                          t_counter[0], stream=stream)
-        if events is not None:
-            events["adam"][1].record(stream)
+                events[i][1].record(stream)
+        return ops
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -157,68 +203,61 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    per_step = [{"reduce": [(ev(), ev()) for _ in buckets], "adam": (ev(), ev())}
-                for _ in range(args.steps)]
+    n_ops = len(launches(1))
+    per_step = [[(ev(), ev()) for _ in range(n_ops)] for _ in range(args.steps)]
     start, end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
+    ops = None
     for k in range(args.steps):
-        step(per_step[k])
+        ops = step(per_step[k])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    red_ms = [sum(a.elapsed_time(b) for a, b in e["reduce"]) for e in per_step]
-    adam_ms = [e["adam"][0].elapsed_time(e["adam"][1]) for e in per_step]
-    n_red_launch = len(buckets) * args.steps
-
-    # algorithmic bytes: reduce reads 2 Nd and writes 4 bytes per owned element;
-    # Adam reads g, master, m, v and writes master, m, v and the fp16 slot.
-    g_bytes = 4 if grad.dtype == torch.float32 else 2     # gradient shard element
-    red_bytes = S * (2 * w.nd + g_bytes) if buckets else 0
-    adam_bytes = S * (26 + g_bytes)
     ms_step = total_ms / args.steps
+
+    # ---- per-kernel figures from the per-launch events ------------------------------------
+    names = {"reduce": "reduce_kernel", "adam": "adam_vec_kernel", "gather": "copy_kernel"}
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
-    red_avg = sum(red_ms) / args.steps
-    adam_avg = sum(adam_ms) / args.steps
-    kernels = {
-        "adam": {"kernel": "adam_vec_kernel", "launches_per_step": 1,
-                 "avg_ms": adam_avg, "min_ms": min(adam_ms),
-                 "bytes_per_launch": adam_bytes, "bytes_per_element": adam_bytes / S,
-                 "gbs": gbs(adam_bytes, adam_avg),
-                 "frac_of_peak": gbs(adam_bytes, adam_avg) / PEAK_HBM_GBS,
-                 "params_per_s": S / (adam_avg * 1e-3)},
-    }
-    if buckets:
-        kernels["reduce"] = {
-            "kernel": "reduce_kernel", "launches_per_step": len(buckets),
-            "avg_ms_per_launch": sum(red_ms) / n_red_launch, "avg_ms_per_step": red_avg,
-            "bytes_per_step": red_bytes, "bytes_per_element": 2 * w.nd + g_bytes,
-            "gbs": gbs(red_bytes, red_avg), "frac_of_peak": gbs(red_bytes, red_avg) / PEAK_HBM_GBS,
-            "params_per_s": S / (red_avg * 1e-3)}
-    dom = max(kernels, key=lambda k: kernels[k].get("avg_ms_per_step", kernels[k].get("avg_ms")))
+    kernels = {}
+    for kind in dict.fromkeys(k for k, _, _ in ops):
+        idx = [i for i, (k, _, _) in enumerate(ops) if k == kind]
+        bytes_step = sum(ops[i][1] for i in idx)
+        per = [sum(per_step[s][i][0].elapsed_time(per_step[s][i][1]) for i in idx)
+               for s in range(args.steps)]
+        avg_step = sum(per) / args.steps
+        kernels[kind] = {
+            "kernel": names[kind], "launches_per_step": len(idx),
+            "avg_ms_per_launch": avg_step / len(idx), "avg_ms_per_step": avg_step,
+            "min_ms_per_step": min(per), "bytes_per_step": bytes_step,
+            "bytes_per_element": bytes_step / S,
+            "gbs": gbs(bytes_step, avg_step), "frac_of_peak": gbs(bytes_step, avg_step) / PEAK_HBM_GBS,
+            "params_per_s": S / (avg_step * 1e-3)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms_per_step"])
     dk = kernels[dom]
-    dom_launch_ms = dk.get("avg_ms_per_launch", dk.get("avg_ms"))
-    dom_launch_bytes = (red_bytes / len(buckets)) if dom == "reduce" else adam_bytes
-    roofline = {"bound": "hbm", "kernel": dk["kernel"],
-                "achieved": dom_launch_bytes / (dom_launch_ms * 1e-3) / 1e9,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": dom_launch_bytes / (dom_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    dom_launch_bytes = dk["bytes_per_step"] / dk["launches_per_step"]
+    achieved = gbs(dom_launch_bytes, dk["avg_ms_per_launch"])
+    roofline = {"bound": "hbm", "kernel": dk["kernel"], "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": measured_traffic(dk["kernel"], w.name),
                 "algorithmic_bytes_per_launch": dom_launch_bytes}
 
     # ---- sampled self-check against the oracle (untimed) --------------------------------
     parity = None
     if init_idx is not None:
-        parity = self_check(w, geom, buckets, grad, master, m, v, param16, init_idx,
-                            t_counter[0])
+        parity = self_check(w, geom, buckets, grad, master, m, v, param16, param16_origin,
+                            init_idx, t_counter[0])
+        if stage3:
+            parity.update(gather_check(w, geom, shards, layer_buf, init_idx, t_counter[0],
+                                       stream))
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, geom, args.cpu_chunk, args.cpu_seconds)
 
-    step_bytes = red_bytes + adam_bytes
+    step_bytes = sum(k["bytes_per_step"] for k in kernels.values())
     out = {
         "metric": METRIC,
         "value": S / (ms_step * 1e-3),
@@ -232,10 +271,13 @@ def main():
         "hbm_frac_of_peak": gbs(step_bytes, ms_step) / PEAK_HBM_GBS,
         "bytes_per_step": step_bytes,
         "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
+                   "stage": 3 if stage3 else (1 if w.nd == 1 else 2),
                    "shard_elements": S, "buckets_in_shard": len(buckets),
-                   "bucket_elements": wl.BUCKET, "grad": "fp16 rows" if buckets else "fp16",
+                   "bucket_elements": wl.BUCKET if not stage3 else "layer",
+                   "grad": "fp16 rows" if buckets else "fp16",
                    "grad_shard": ("fp32" if g_bytes == 4 else "fp16") if buckets else None,
-                   "state": "fp32 master/m/v", "slot": "fp16"},
+                   "state": "fp32 master/m/v",
+                   "slot": "own fp16 shard" if stage3 else "fp16 flat vector"},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -244,7 +286,8 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-KERNEL_SOURCES = {"reduce_kernel": "reduce_shard.hip", "adam_vec_kernel": "adam_step_shard.hip"}
+KERNEL_SOURCES = {"reduce_kernel": "reduce_shard.hip", "adam_vec_kernel": "adam_step_shard.hip",
+                  "copy_kernel": "gather_params.hip"}
 
 
 def kernel_source_sha256(kernel):
@@ -274,39 +317,48 @@ def measured_traffic(kernel, workload_name):
         return None
 
 
-def self_check(w, geom, buckets, grad, master, m, v, param16, idx, steps_done):
-    """Sampled comparison with the oracle: the reduced gradient bit for bit, and the
-    state after all the bench's Adam steps, stepped by the oracle from the same
-    initial values."""
-    import torch
+def _oracle_after(w, flat, steps_done, buckets, fp16_shard):
+    """The oracle at flat indices of the shard: the reduced gradient (fp32, or its
+    fp16 bits for an fp16 shard; the raw fp16 gradient without buckets) and the
+    state after `steps_done` Adam steps from the seeded initial state."""
     from oracle import adam as oadam
     from oracle import reduce as ored
     from synth import gen
-    flat = idx.astype(np.uint64) + np.uint64(geom.offset)
-    it = torch.from_numpy(idx.astype(np.int64)).to(grad.device)
     if buckets:
         rows = np.stack([gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
                          for k in range(w.nd)])
         g_ref = ored.reduce_values(rows, w.nd)
-        if grad.dtype == torch.float32:
-            g_dev = grad.index_select(0, it).cpu().numpy()
-            reduce_ok = bool(np.array_equal(g_ref.view(np.uint32), g_dev.view(np.uint32)))
-        else:
-            g_ref = g_ref.astype(np.float16).view(np.uint16)      # the fp16 gradient shard
-            g_dev = grad.index_select(0, it).cpu().numpy().view(np.uint16)
-            reduce_ok = bool(np.array_equal(g_ref, g_dev))
+        if fp16_shard:
+            g_ref = g_ref.astype(np.float16).view(np.uint16)
     else:
         g_ref = gen.grad_f16(w.seed, 0, flat, w.grad.sigma, w.grad.heavy_tail,
                              kind=gen.KIND_GRAD_FULL)
-        reduce_ok = None
     th = gen.state_f32(w.seed, gen.KIND_MASTER, flat, w.master.sigma)
     mm = gen.state_f32(w.seed, gen.KIND_M, flat, w.m.sigma, w.m.absolute)
     vv = gen.state_f32(w.seed, gen.KIND_V, flat, w.v.sigma, w.v.absolute)
+    p16 = None
     for t in range(1, steps_done + 1):
         th, mm, vv, p16 = oadam.step_values(th, mm, vv, g_ref,
                                             oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, t))
+    return g_ref, th, mm, vv, p16
+
+
+def self_check(w, geom, buckets, grad, master, m, v, param16, param16_origin, idx, steps_done):
+    """Sampled comparison with the oracle: the reduced gradient bit for bit, and the
+    state after all the bench's Adam steps, stepped by the oracle from the same
+    initial values."""
+    import torch
+    flat = idx.astype(np.uint64) + np.uint64(geom.offset)
+    it = torch.from_numpy(idx.astype(np.int64)).to(grad.device)
+    fp16_shard = grad.dtype != torch.float32
+    g_ref, th, mm, vv, p16 = _oracle_after(w, flat, steps_done, buckets, fp16_shard)
+    reduce_ok = None
+    if buckets:
+        g_dev = grad.index_select(0, it).cpu().numpy()
+        reduce_ok = bool(np.array_equal(g_ref.view(np.uint16 if fp16_shard else np.uint32),
+                                        g_dev.view(np.uint16 if fp16_shard else np.uint32)))
     got = [x.index_select(0, it).cpu().numpy() for x in (master, m, v)]
-    pi = torch.from_numpy((idx + geom.offset).astype(np.int64)).to(grad.device)
+    pi = torch.from_numpy((idx + geom.offset - param16_origin).astype(np.int64)).to(grad.device)
     got_p = param16.index_select(0, pi).cpu().numpy().view(np.uint16)
     adam_ok = all(np.array_equal(a.view(np.uint32), b.view(np.uint32))
                   for a, b in zip(got, (th, mm, vv))) and np.array_equal(got_p, p16)
@@ -316,6 +368,42 @@ def self_check(w, geom, buckets, grad, master, m, v, param16, idx, steps_done):
     return {"samples": int(idx.size), "adam_steps": steps_done,
             "reduce_bit_exact": reduce_ok, "adam_bit_exact": bool(adam_ok),
             "adam_max_rel_err": rel}
+
+
+def gather_check(w, geom, shards, layer_buf, idx, steps_done, stream):
+    """Stage 3: gather (untimed) the layer holding the end of the rank's shard and
+    compare sampled elements with the oracle: inside the shard, the fp16
+    parameters after the bench's Adam steps; elsewhere, the other ranks' shards
+    as generated."""
+    import torch
+    import zero_sharded_mixed_bucketed_amd as Z
+    from synth import gen
+    last = geom.offset + geom.len - 1
+    off, n = next((o, k) for o, k in w.buckets if o <= last < o + k)
+    with torch.cuda.stream(stream):
+        Z.gather_params(w.psi, w.nd, off, n, shards, layer_buf[:n], stream=stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rel = np.unique(np.concatenate([np.arange(min(64, n)), np.arange(max(0, n - 64), n),
+                                    np.clip(np.arange(last - off - 63, last - off + 65), 0, n - 1),
+                                    rng.integers(0, n, size=idx.size)])).astype(np.int64)
+    flat = (rel + off).astype(np.uint64)
+    got = layer_buf.index_select(0, torch.from_numpy(rel).to(layer_buf.device)).cpu().numpy() \
+        .view(np.uint16)
+    # each gathered element is its owner's current fp16 parameter: inside this
+    # rank's shard, the oracle's after the Adam steps; elsewhere, as generated
+    s_all = -(-w.psi // w.nd)
+    owner = (flat // np.uint64(s_all)).astype(np.int64)
+    want = np.empty(flat.size, np.uint16)
+    mine = owner == geom.rank
+    if mine.any():
+        want[mine] = _oracle_after(w, flat[mine], steps_done, True, True)[4]
+    for k in np.unique(owner[~mine]):
+        sel = owner == k
+        want[sel] = gen.grad_f16(w.seed, int(k), flat[sel], w.extra["param_sigma"],
+                                 kind=gen.KIND_PARAM16)
+    return {"gather_samples": int(rel.size), "gather_bit_exact": bool(np.array_equal(got, want)),
+            "gather_layer": [int(off), int(n)]}
 
 
 def _oracle_inputs(args):

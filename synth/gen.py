@@ -44,6 +44,7 @@ KIND_MASTER = 2     # fp32 master weights
 KIND_M = 3          # fp32 first moment
 KIND_V = 4          # fp32 second moment
 KIND_GRAD_FULL = 5  # fp16 gradient of a plain data-parallel (Nd = 1) run
+KIND_PARAM16 = 6    # fp16 parameters held in a stage-3 rank shard
 
 # Heavy-tail thresholds on the 16-bit uniform (about 1% zeros, 1% outliers).
 TAIL_ZERO_BELOW = 655

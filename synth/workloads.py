@@ -140,6 +140,18 @@ def zero2_7p5b_g16(rank: int = 0) -> Workload:
                        "grad_shard": "fp16"})
 
 
+def zero3_7p5b(rank: int = 0) -> Workload:
+    """Stage-3 rank of the 7.5B model at Nd = 64: hidden 4096 (37 layers of
+    12 h^2 + 2 h and a truncated last one), each layer's parameters gathered in
+    forward and in backward, the layer gradients reduced per layer, an fp16
+    gradient shard."""
+    w = zero2_7p5b(rank)
+    return Workload(**{**w.__dict__, "name": f"zero3-7.5B-nd64-r{rank}",
+                       "buckets": tuple(reversed(transformer_layers(w.psi, 4096))),
+                       "grad_shard": "fp16",
+                       "extra": {"stage": 3, "hidden": 4096, "param_sigma": 0.02}})
+
+
 def zero2_13b(rank: int = 0) -> Workload:
     """ZeRO-2 rank of a 13B model at Nd = 32 with heavy-tailed gradients."""
     psi = 13_000_000_000
