@@ -8,13 +8,15 @@
 //
 // Flat index i lives in rank k = i / S's shard at position i - k S.  A layer's
 // range crosses one shard or a few, so the host splits it into per-rank pieces,
-// each a contiguous copy, and launches one copy per piece.  A piece is copied
-// with the widest access the source and destination allow together (16, 8, 4
-// or 2 bytes, from their alignment relative to each other); the elements
-// before the destination reaches that alignment and after the last full vector
-// go element by element in the same launch.  Pure data movement, bit-exact.
-// When a range crosses many small shards an element-wise kernel does the whole
-// range in one launch.
+// each a contiguous copy, and one launch copies them all: every workgroup
+// belongs to one piece (a table of at most kMaxGatherPieces in the kernel
+// arguments).  A piece is copied with the widest access its source and
+// destination allow together (16, 8, 4 or 2 bytes, from their alignment
+// relative to each other); the elements before the destination reaches that
+// alignment and after the last full vector go element by element.  The width
+// is uniform within a workgroup.  Pure data movement, bit-exact.  When a
+// range crosses more shards than the table holds, an element-wise kernel does
+// the whole range in one launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,36 +30,46 @@ constexpr int kThreads = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int kW>
-struct Vec;
-template <>
-struct Vec<16> { typedef u32x4 T; };
-template <>
-struct Vec<8> { typedef u32x2 T; };
-template <>
-struct Vec<4> { typedef uint32_t T; };
+struct Piece {
+  const uint16_t* src;
+  uint16_t* dst;
+  uint64_t n;         // elements
+  uint64_t head;      // elements before dst reaches the access width
+  uint64_t nvec;      // full vectors after the head
+  uint32_t block0;    // first workgroup of this piece
+  uint32_t width;     // bytes per access: 16, 8, 4 or 2
+};
 
-// Elements [0, head) and [head + nvec * V, n) element by element, the vectors
-// in between with kW-byte accesses (V = kW / 2 elements each).
-template <int kW>
-__global__ void __launch_bounds__(kThreads) copy_kernel(const uint16_t* src, uint16_t* dst,
-                                                        uint64_t n, uint64_t head,
-                                                        uint64_t nvec) {
-  const uint64_t t = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if constexpr (kW > 2) {
-    constexpr uint64_t V = kW / 2;
-    typedef typename Vec<kW>::T VT;
-    if (t < nvec) {
-      const uint64_t e = head + t * V;
-      const VT x = __builtin_nontemporal_load(reinterpret_cast<const VT*>(src + e));
-      __builtin_nontemporal_store(x, reinterpret_cast<VT*>(dst + e));
-      return;
-    }
-    const uint64_t r = t - nvec;                      // a head or tail element
-    const uint64_t e = r < head ? r : head + nvec * V + (r - head);
-    if (e < n) dst[e] = src[e];
-  } else {
-    if (t < n) dst[t] = src[t];
+struct Pieces {
+  Piece p[kMaxGatherPieces];
+  uint32_t count;
+};
+
+template <typename VT, int kV>
+__device__ __forceinline__ void copy_piece(const Piece& pc, uint64_t t) {
+  if (t < pc.nvec) {
+    const uint64_t e = pc.head + t * kV;
+    const VT x = __builtin_nontemporal_load(reinterpret_cast<const VT*>(pc.src + e));
+    __builtin_nontemporal_store(x, reinterpret_cast<VT*>(pc.dst + e));
+    return;
+  }
+  const uint64_t r = t - pc.nvec;                     // a head or tail element
+  const uint64_t e = r < pc.head ? r : pc.head + pc.nvec * kV + (r - pc.head);
+  if (e < pc.n) pc.dst[e] = pc.src[e];
+}
+
+__global__ void __launch_bounds__(kThreads) copy_kernel(Pieces ps) {
+  uint32_t q = 0;                                     // this workgroup's piece
+  while (q + 1 < ps.count && blockIdx.x >= ps.p[q + 1].block0) ++q;
+  const Piece& pc = ps.p[q];
+  const uint64_t t = static_cast<uint64_t>(blockIdx.x - pc.block0) * kThreads + threadIdx.x;
+  switch (pc.width) {
+    case 16: copy_piece<u32x4, 8>(pc, t); break;
+    case 8: copy_piece<u32x2, 4>(pc, t); break;
+    case 4: copy_piece<uint32_t, 2>(pc, t); break;
+    default:
+      if (t < pc.n) pc.dst[t] = pc.src[t];
+      break;
   }
 }
 
@@ -70,27 +82,18 @@ __global__ void __launch_bounds__(kThreads) gather_elem_kernel(GatherLaunch a) {
   a.out[j] = a.shards[k * a.stride + (i - k * a.s)];
 }
 
-hipError_t copy_piece(const uint16_t* src, uint16_t* dst, uint64_t n, hipStream_t stream) {
-  const uintptr_t rel = (reinterpret_cast<uintptr_t>(src) - reinterpret_cast<uintptr_t>(dst));
-  const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
-  int w = (rel % 16 == 0) ? 16 : (rel % 8 == 0) ? 8 : (rel % 4 == 0) ? 4 : 2;
-  uint64_t head = 0, nvec = 0;
-  if (w > 2) {
-    head = ((w - d % w) % w) / 2;                    // elements until dst is w-aligned
-    if (head > n) head = n;
-    nvec = (n - head) / (w / 2);
-  }
-  const uint64_t work = w > 2 ? nvec + (n - nvec * (w / 2)) : n;   // vectors + loose elements
-  const uint64_t blocks = (work + kThreads - 1) / kThreads;
-  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  switch (w) {
-    case 16: hipLaunchKernelGGL(copy_kernel<16>, grid, dim3(kThreads), 0, stream, src, dst, n, head, nvec); break;
-    case 8: hipLaunchKernelGGL(copy_kernel<8>, grid, dim3(kThreads), 0, stream, src, dst, n, head, nvec); break;
-    case 4: hipLaunchKernelGGL(copy_kernel<4>, grid, dim3(kThreads), 0, stream, src, dst, n, head, nvec); break;
-    default: hipLaunchKernelGGL(copy_kernel<2>, grid, dim3(kThreads), 0, stream, src, dst, n, head, nvec); break;
-  }
-  return hipGetLastError();
+// Fills one piece's access width, head, vector count and thread count.
+uint64_t plan_piece(Piece& pc) {
+  const uintptr_t rel = reinterpret_cast<uintptr_t>(pc.src) - reinterpret_cast<uintptr_t>(pc.dst);
+  const uintptr_t d = reinterpret_cast<uintptr_t>(pc.dst);
+  const uint32_t w = (rel % 16 == 0) ? 16 : (rel % 8 == 0) ? 8 : (rel % 4 == 0) ? 4 : 2;
+  pc.width = w;
+  pc.head = pc.nvec = 0;
+  if (w == 2) return pc.n;
+  pc.head = ((w - d % w) % w) / 2;                    // elements until dst is w-aligned
+  if (pc.head > pc.n) pc.head = pc.n;
+  pc.nvec = (pc.n - pc.head) / (w / 2);
+  return pc.nvec + (pc.n - pc.nvec * (w / 2));        // vectors + loose elements
 }
 
 }  // namespace
@@ -105,14 +108,24 @@ hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
+  Pieces ps;
+  ps.count = 0;
+  uint64_t blocks = 0;
   for (uint64_t k = k_first; k <= k_last; ++k) {
     const uint64_t p_lo = k * a.s > a.lo ? k * a.s : a.lo;
     const uint64_t p_hi = (k + 1) * a.s < a.lo + a.n ? (k + 1) * a.s : a.lo + a.n;
-    const hipError_t e = copy_piece(a.shards + k * a.stride + (p_lo - k * a.s),
-                                    a.out + (p_lo - a.lo), p_hi - p_lo, stream);
-    if (e != hipSuccess) return e;
+    Piece& pc = ps.p[ps.count++];
+    pc.src = a.shards + k * a.stride + (p_lo - k * a.s);
+    pc.dst = a.out + (p_lo - a.lo);
+    pc.n = p_hi - p_lo;
+    const uint64_t work = plan_piece(pc);
+    pc.block0 = static_cast<uint32_t>(blocks);
+    blocks += (work + kThreads - 1) / kThreads;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     ps);
+  return hipGetLastError();
 }
 
 }  // namespace zero
