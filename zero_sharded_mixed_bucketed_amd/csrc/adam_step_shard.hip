@@ -27,6 +27,7 @@ namespace zero {
 namespace {
 
 constexpr int kThreads = 64;    // one wavefront per workgroup
+constexpr int kWgsPerCu = 10;   // occupancy cap of the vector kernel
 constexpr int kVec = 4;         // elements per thread (16-byte accesses of the fp32 arrays)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -102,7 +103,10 @@ __device__ __forceinline__ void store_p16(const Args& a, uint64_t j, const f32x4
 // One group of 4 elements per thread and a grid that covers the shard: on
 // MI355X this streams the 4-read/4-write mix faster than a grid-stride loop
 // with fewer, larger workgroups (short-lived wave-sized workgroups keep every
-// CU refilled and the live accesses in one moving window of memory).
+// CU refilled and the live accesses in one moving window of memory).  The
+// launch caps a CU at 10 such workgroups (dynamic LDS the kernel never
+// touches): with fewer concurrent streams per CU the mix runs at 6.55 rather
+// than 6.0 TB/s.
 template <bool kG16>
 __global__ void __launch_bounds__(kThreads) adam_vec_kernel(Args a) {
   const uint64_t gi = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(kThreads) adam_scalar_kernel(Args a, uint64_t 
 
 }  // namespace
 
-hipError_t launch_adam(const AdamLaunch& L, int cus, hipStream_t stream) {
+hipError_t launch_adam(const AdamLaunch& L, const DeviceInfo& d, hipStream_t stream) {
   Args a;
   a.master = L.master;
   a.m = L.m;
@@ -171,10 +175,11 @@ hipError_t launch_adam(const AdamLaunch& L, int cus, hipStream_t stream) {
     const uint64_t want = (a.ngroups + kThreads - 1) / kThreads;
     if (want > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const unsigned blocks = static_cast<unsigned>(want);
+    const unsigned cap = occupancy_cap_bytes(d, kWgsPerCu);
     if (L.grad_is_fp16)
-      hipLaunchKernelGGL(adam_vec_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(adam_vec_kernel<true>, dim3(blocks), dim3(kThreads), cap, stream, a);
     else
-      hipLaunchKernelGGL(adam_vec_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(adam_vec_kernel<false>, dim3(blocks), dim3(kThreads), cap, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -183,7 +188,7 @@ hipError_t launch_adam(const AdamLaunch& L, int cus, hipStream_t stream) {
     const uint64_t rest = L.n - first;
     // the tail (< 4 elements) or a whole misaligned shard: grid-stride over it
     const uint64_t want_s = (rest + kThreads - 1) / kThreads;
-    const uint64_t cap = static_cast<uint64_t>(cus) * 32;
+    const uint64_t cap = static_cast<uint64_t>(d.cus) * 32;
     const unsigned blocks = static_cast<unsigned>(want_s < cap ? want_s : cap);
     if (L.grad_is_fp16)
       hipLaunchKernelGGL(adam_scalar_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a,

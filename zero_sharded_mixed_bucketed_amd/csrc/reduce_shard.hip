@@ -9,10 +9,12 @@
 // no reuse), so it is built for streaming: each thread owns 8 consecutive
 // columns, reads each row's 8 fp16 values with one 16-byte load (narrower
 // only when the row stride or base rules 16 bytes out), keeps the 8 running
-// sums in registers, and issues the loads of a batch of 32 rows before adding
-// them, so that 512 bytes per thread are in flight; the rows left over after
-// the last full batch go in batches of 16, 8, 4, 2 and 1.  A workgroup is one
-// wavefront and reads 1 KiB contiguous per row.  Vectorisation is across
+// sums in registers, and takes the rows in batches of 16 (the rows left over
+// after the last full batch in batches of 8, 4, 2 and 1), with the loads of a
+// batch overlapping the additions of the rows before.  A workgroup is one
+// wavefront and reads 1 KiB contiguous per row.  At most 8 workgroups share a
+// compute unit (a dynamic-LDS occupancy cap): fewer concurrent row streams
+// per CU move more bytes per second on MI355X (6.5 against 6.1 TB/s at Nd = 64).  Vectorisation is across
 // elements, never across ranks, so each element's additions keep the rank
 // order and the result is bit-exact.  A thread reads every row of its
 // columns before it writes their outputs, and no other thread touches those
@@ -20,10 +22,8 @@
 // reduced value replacing that row's element in place).
 //
 // On MI355X a pure 64-row read of this shape streams at about 7.2 TB/s; the
-// 4 bytes per element written back cost the rest (writes that leave L2 while
-// the read stream saturates HBM are expensive), which is why the grid is made
-// of short-lived one-wave workgroups with deep load batches rather than fewer,
-// longer-lived ones.
+// 4 bytes per element written back cost most of the rest (writes that leave
+// L2 while the read stream saturates HBM are expensive).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,7 +36,8 @@ namespace {
 
 constexpr int kThreads = 64;  // one wavefront per workgroup
 constexpr int kCols = 8;      // columns per thread (one 16-byte fp16 load per row)
-constexpr int kBatch = 32;    // rows loaded before they are added
+constexpr int kBatch = 16;    // rows loaded before they are added
+constexpr int kWgsPerCu = 8;  // occupancy cap
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -164,9 +165,13 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
   if (c >= a.c_lo && c + kCols <= a.c_hi) {
     const uint16_t* p = a.rows + c;
     uint32_t k = 0;
-    for (; k + kBatch <= a.nd; k += kBatch) add_rows<kW, kBatch>(acc, p, k, a.stride);
-    // the remaining nd % 32 rows, still in ascending order
-    if (a.nd - k >= 16) { add_rows<kW, 16>(acc, p, k, a.stride); k += 16; }
+    // The bound is computed once: with it the compiler knows the trip count and
+    // overlaps each batch's loads with the previous rows' additions (6 or 7 loads
+    // in flight throughout), which streams about 5% faster than issuing the 16
+    // loads of a batch at once and draining them.
+    const uint32_t nfull = a.nd - a.nd % kBatch;
+    for (; k < nfull; k += kBatch) add_rows<kW, kBatch>(acc, p, k, a.stride);
+    // the remaining nd % 16 rows, still in ascending order
     if (a.nd - k >= 8) { add_rows<kW, 8>(acc, p, k, a.stride); k += 8; }
     if (a.nd - k >= 4) { add_rows<kW, 4>(acc, p, k, a.stride); k += 4; }
     if (a.nd - k >= 2) { add_rows<kW, 2>(acc, p, k, a.stride); k += 2; }
@@ -202,7 +207,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
 
 }  // namespace
 
-hipError_t launch_reduce(const ReduceLaunch& L, int /*cus*/, hipStream_t stream) {
+hipError_t launch_reduce(const ReduceLaunch& L, const DeviceInfo& d, hipStream_t stream) {
   Args a;
   a.rows = L.rows;
   a.stride = L.stride;
@@ -235,11 +240,12 @@ hipError_t launch_reduce(const ReduceLaunch& L, int /*cus*/, hipStream_t stream)
   const uint64_t blocks = (a.ngroups + kThreads - 1) / kThreads;
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
+  const unsigned cap = occupancy_cap_bytes(d, kWgsPerCu);
   switch (w) {
-    case 16: hipLaunchKernelGGL(reduce_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(reduce_kernel<16>, grid, dim3(kThreads), cap, stream, a); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(kThreads), cap, stream, a); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(kThreads), cap, stream, a); break;
+    default: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(kThreads), cap, stream, a); break;
   }
   return hipGetLastError();
 }

@@ -28,27 +28,36 @@ int ok() {
   return ZERO_OK;
 }
 
-// Compute-unit count of the current device, looked up once per device.
+// Compute units and LDS bytes per compute unit of the current device, looked
+// up once per device.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_lds[kMaxDevices];
 
-int device_cus(int* cus) {
+int device_info(zero::DeviceInfo* info) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(ZERO_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices) {
-    *cus = 256;
+    info->cus = 256;
+    info->lds_per_cu = 160 * 1024;
     return ZERO_OK;
   }
   int c = g_cus[dev].load(std::memory_order_relaxed);
-  if (c <= 0) {
+  int l = g_lds[dev].load(std::memory_order_relaxed);
+  if (c <= 0 || l <= 0) {
     e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e != hipSuccess)
       return fail(ZERO_E_DEVICE, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
     if (c <= 0) c = 256;
+    if (l <= 0) l = 160 * 1024;
     g_cus[dev].store(c, std::memory_order_relaxed);
+    g_lds[dev].store(l, std::memory_order_relaxed);
   }
-  *cus = c;
+  info->cus = c;
+  info->lds_per_cu = l;
   return ZERO_OK;
 }
 
@@ -200,8 +209,8 @@ int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t buc
     return fail(ZERO_E_RANGE, "slice buffer size overflows");
   if (!aligned(slices, 2) || (grad32 && !aligned(grad32, 4)) || (grad16 && !aligned(grad16, 2)))
     return fail(ZERO_E_ALIGN, "slices/grad16 need 2-byte and grad32 4-byte alignment");
-  int cus = 0;
-  if ((rc = device_cus(&cus))) return rc;
+  zero::DeviceInfo dinfo;
+  if ((rc = device_info(&dinfo))) return rc;
   zero::ReduceLaunch L;
   L.rows = slices;
   L.stride = slice_stride;
@@ -213,7 +222,7 @@ int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t buc
   L.out32 = grad32;
   L.out16 = grad16;
   L.inv_nd = 1.0f / static_cast<float>(g->nd);
-  hipError_t e = zero::launch_reduce(L, cus, static_cast<hipStream_t>(hip_stream));
+  hipError_t e = zero::launch_reduce(L, dinfo, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(ZERO_E_DEVICE, "reduce launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -248,8 +257,8 @@ int zero_adam_step_shard(const zero_geom_t* g, const zero_shard_t* s, double lr,
   if (!aligned(s->master, 4) || !aligned(s->m, 4) || !aligned(s->v, 4) ||
       !aligned(s->grad, s->grad_is_fp16 ? 2 : 4) || (s->param16 && !aligned(s->param16, 2)))
     return fail(ZERO_E_ALIGN, "fp32 arrays need 4-byte, fp16 arrays 2-byte alignment");
-  int cus = 0;
-  if ((rc = device_cus(&cus))) return rc;
+  zero::DeviceInfo dinfo;
+  if ((rc = device_info(&dinfo))) return rc;
   float sc[7];
   derive_scalars(lr, beta1, beta2, eps, step, sc);
   zero::AdamLaunch L;
@@ -267,7 +276,7 @@ int zero_adam_step_shard(const zero_geom_t* g, const zero_shard_t* s, double lr,
   L.eps = sc[4];
   L.step = sc[5];
   L.isb = sc[6];
-  hipError_t e = zero::launch_adam(L, cus, static_cast<hipStream_t>(hip_stream));
+  hipError_t e = zero::launch_adam(L, dinfo, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(ZERO_E_DEVICE, "adam launch: %s", hipGetErrorString(e));
   return ok();
 }
