@@ -78,8 +78,9 @@ def test_memory_model_rejects():
         Z.memory_model(100, 4, 4)
 
 
-@pytest.mark.parametrize("psi", [1, 7, 37, 1000, 1 << 20, 7_500_000_000, 10 ** 11])
-@pytest.mark.parametrize("nd", [1, 3, 4, 64, 400])
+@pytest.mark.parametrize("psi", [1, 7, 37, 1000, 1 << 20, 7_500_000_000, 10 ** 11,
+                                 2 ** 64 - 1, 2 ** 64 - 3, 2 ** 63 + 5])
+@pytest.mark.parametrize("nd", [1, 3, 4, 7, 64, 400])
 def test_geometry_matches_oracle(psi, nd):
     ranks = range(nd) if nd <= 64 else (0, 1, 137, nd - 1)
     for r in ranks:

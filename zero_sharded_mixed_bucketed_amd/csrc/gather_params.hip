@@ -111,9 +111,11 @@ hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream) {
   Pieces ps;
   ps.count = 0;
   uint64_t blocks = 0;
+  const uint64_t end = a.lo + a.n;                    // <= psi: checked by the caller
   for (uint64_t k = k_first; k <= k_last; ++k) {
-    const uint64_t p_lo = k * a.s > a.lo ? k * a.s : a.lo;
-    const uint64_t p_hi = (k + 1) * a.s < a.lo + a.n ? (k + 1) * a.s : a.lo + a.n;
+    const uint64_t base = k * a.s;                     // <= lo + n - 1: no overflow
+    const uint64_t p_lo = base > a.lo ? base : a.lo;
+    const uint64_t p_hi = end - base > a.s ? base + a.s : end;
     Piece& pc = ps.p[ps.count++];
     pc.src = a.shards + k * a.stride + (p_lo - k * a.s);
     pc.dst = a.out + (p_lo - a.lo);

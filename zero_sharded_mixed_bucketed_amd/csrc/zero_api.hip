@@ -63,17 +63,17 @@ int device_info(zero::DeviceInfo* info) {
 
 void geometry(uint64_t psi, uint32_t nd, uint32_t rank, zero_geom_t* out) {
   const uint64_t s = psi / nd + (psi % nd != 0);
-  // r * s can exceed psi only for trailing ranks; no overflow since r < nd and
-  // s <= psi / nd + 1.
-  uint64_t lo = static_cast<uint64_t>(rank) * s;
-  uint64_t hi = lo + s;
+  // lo = min(rank * S, psi) and hi = lo + min(S, psi - lo), computed without
+  // overflow: for psi near 2^64, rank * S and (rank + 1) * S can exceed it.
+  uint64_t lo = psi;
+  if (rank == 0 || s <= psi / rank) lo = static_cast<uint64_t>(rank) * s;
   if (lo > psi) lo = psi;
-  if (hi > psi) hi = psi;
+  const uint64_t len = (psi - lo < s) ? psi - lo : s;
   out->psi = psi;
   out->nd = nd;
   out->rank = rank;
   out->offset = lo;
-  out->len = hi - lo;
+  out->len = len;
 }
 
 int check_geom(const zero_geom_t* g) {
