@@ -69,3 +69,39 @@ def test_named_values():
     # 1 + 2^-11 ties between 1 and 1 + 2^-10 -> 1 (even); 1 + 3*2^-11 -> 1 + 2^-9
     assert f32_bits_to_f16_bits(0x3F801000) == 0x3C00
     assert f32_bits_to_f16_bits(0x3F803000) == 0x3C02
+
+
+def _binade_mismatches(args):
+    import numpy as np
+    from fp16_exact import f16_bits_of_binade
+    sign, e = args
+    bits = (np.uint32(sign << 31) | np.uint32(e << 23)) | np.arange(1 << 23, dtype=np.uint32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        got = bits.view(np.float32).astype(np.float16).view(np.uint16)
+    if e == 0xFF:                      # NaN stays NaN (payloads are not compared), inf exact
+        want = f16_bits_of_binade(sign, e)
+        nan = (want & 0x3FF) != 0
+        bad = ((got & 0x7C00) != 0x7C00) | (((got & 0x3FF) != 0) != nan)
+        return int(np.count_nonzero(bad | (~nan & (got != want))))
+    lo = f32_bits_to_f16_bits(int(bits[0]))
+    hi = f32_bits_to_f16_bits(int(bits[-1]))
+    if lo == hi:
+        # rounding is monotone within a binade: equal ends mean the whole binade
+        # maps to that one value (all of +-0 below 2^-25, all of +-inf from 65536)
+        return int(np.count_nonzero(got != lo))
+    return int(np.count_nonzero(got != f16_bits_of_binade(sign, e)))
+
+
+def test_narrowing_exhaustive_all_fp32():
+    """NumPy's fp32 -> fp16 cast (the oracle's) against the integer definition on
+    every one of the 2^32 fp32 bit patterns, one binade (sign, exponent) at a time."""
+    import multiprocessing as mp
+    import os
+    import time
+    jobs = [(s, e) for s in (0, 1) for e in range(256)]
+    t0 = time.time()
+    workers = max(1, min(4, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(workers) as pool:
+        bad = pool.map(_binade_mismatches, jobs, chunksize=8)
+    assert sum(bad) == 0, [(j, b) for j, b in zip(jobs, bad) if b][:5]
+    print(f"2^32 patterns checked in {time.time() - t0:.1f} s with {workers} processes")
