@@ -282,8 +282,18 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "env": environment(torch, dev),
     }
     print(json.dumps(out), flush=True)
+
+
+def environment(torch, dev):
+    """What the numbers were measured on."""
+    p = torch.cuda.get_device_properties(dev)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0))}
 
 
 KERNEL_SOURCES = {"reduce_kernel": "reduce_shard.hip", "adam_vec_kernel": "adam_step_shard.hip",
