@@ -200,3 +200,43 @@ def test_memory_k_mutants_fail_a_pin(monkeypatch, mutation):
         except AssertionError:
             failed += 1
     assert failed, mutation
+
+
+# ---- stage-3 parameter gather ---------------------------------------------------------
+
+import test_oracle_stage3 as pins_stage3  # noqa: E402
+from oracle import geometry as ogeo  # noqa: E402
+from oracle import stage3 as st3  # noqa: E402
+
+
+def _gather(mutation):
+    def gather_params(shards, psi, nd, lo, n):
+        s = ogeo.shard_size(psi, nd)
+        if mutation == "floor_shard_size":
+            s = max(1, psi // nd)
+        i = np.arange(lo, lo + n, dtype=np.int64)
+        k = i // s
+        if mutation == "next_rank":
+            k = np.minimum(k + (i % 7 == 3), nd - 1)
+        k = np.minimum(k, nd - 1)
+        col = i - k * s
+        if mutation == "column_from_range_start":
+            col = col - (lo % s) * (i == lo)
+        return shards[k, np.clip(col, 0, shards.shape[1] - 1)]
+    return gather_params
+
+
+@pytest.mark.parametrize("mutation", ["floor_shard_size", "next_rank", "column_from_range_start"])
+def test_gather_mutants_fail_a_pin(monkeypatch, mutation):
+    monkeypatch.setattr(st3, "gather_params", _gather(mutation))
+    failed = 0
+    checks = [lambda: [pins_stage3.test_all_layers_rebuild_the_vector(psi, nd)
+                       for psi, nd in ((10, 3), (37, 4), (100, 7), (1000, 64))],
+              lambda: [pins_stage3.test_brute_force_owner_scan(psi, nd)
+                       for psi, nd in ((10, 3), (37, 4))]]
+    for fn in checks:
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    assert failed, mutation

@@ -5,25 +5,28 @@
 //
 // Nd fp16 rows, one per data-parallel rank, are summed element by element in
 // fp32, in ascending rank order starting from +0, and scaled once by RN32(1/Nd).
-// The kernel is HBM-bound (2 Nd bytes read and 4 written per output element,
-// no reuse), so it is built for streaming: each thread owns 8 consecutive
-// columns, reads each row's 8 fp16 values with one 16-byte load (narrower
-// only when the row stride or base rules 16 bytes out), keeps the 8 running
-// sums in registers, and takes the rows in batches of 16 (the rows left over
-// after the last full batch in batches of 8, 4, 2 and 1), with the loads of a
-// batch overlapping the additions of the rows before.  A workgroup is one
-// wavefront and reads 1 KiB contiguous per row.  At most 8 workgroups share a
-// compute unit (a dynamic-LDS occupancy cap): fewer concurrent row streams
-// per CU move more bytes per second on MI355X (6.5 against 6.1 TB/s at Nd = 64).  Vectorisation is across
-// elements, never across ranks, so each element's additions keep the rank
-// order and the result is bit-exact.  A thread reads every row of its
-// columns before it writes their outputs, and no other thread touches those
-// columns, so an output may share memory with a row column for column (the
-// reduced value replacing that row's element in place).
+// Vectorisation is across elements, never across ranks, so each element's
+// additions keep the rank order and the result is bit-exact.
 //
-// On MI355X a pure 64-row read of this shape streams at about 7.2 TB/s; the
-// 4 bytes per element written back cost most of the rest (writes that leave
-// L2 while the read stream saturates HBM are expensive).
+// The kernel is HBM-bound (2 Nd bytes read and 4 written per output element,
+// no reuse) and built for streaming:
+//  - each thread owns 8 consecutive columns and reads each row's 8 fp16 values
+//    with one 16-byte non-temporal load (narrower only when the row stride or
+//    base rules 16 bytes out), keeping the 8 running sums in registers;
+//  - the rows go in batches of 16 (the rest in batches of 8, 4, 2 and 1), and
+//    each batch's loads overlap the additions of the rows before it, so 6 or 7
+//    loads per thread are in flight throughout;
+//  - a workgroup is one wavefront and reads 1 KiB contiguous per row;
+//  - at most 8 workgroups share a compute unit (a dynamic-LDS occupancy cap set
+//    at launch): fewer concurrent row streams per CU move more bytes per second
+//    on MI355X (6.4 against 6.1 TB/s at Nd = 64).
+// On MI355X the same access pattern without the stores streams at about
+// 7.0 TB/s under the cap; the 4 bytes per element written back cost the rest
+// (writes that leave L2 while the read stream saturates HBM are expensive).
+//
+// A thread reads every row of its columns before it writes their outputs, and
+// no other thread touches those columns, so an output may share memory with a
+// row column for column (the reduced value replacing that row's element).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,7 +39,7 @@ namespace {
 
 constexpr int kThreads = 64;  // one wavefront per workgroup
 constexpr int kCols = 8;      // columns per thread (one 16-byte fp16 load per row)
-constexpr int kBatch = 16;    // rows loaded before they are added
+constexpr int kBatch = 16;    // rows per batch
 constexpr int kWgsPerCu = 8;  // occupancy cap
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -141,8 +144,9 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* p) {
   }
 }
 
-// Adds rows [k, k + kB) at the thread's 8 columns: all kB loads are issued
-// before the first addition, then the rows are added in ascending order.
+// Adds rows [k, k + kB) at the thread's 8 columns, in ascending order (the
+// loads are independent of each other; the compiler overlaps them with the
+// additions).
 template <int kW, int kB>
 __device__ __forceinline__ void add_rows(float (&acc)[kCols], const uint16_t* p, uint32_t k,
                                          uint64_t stride) {
