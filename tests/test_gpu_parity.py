@@ -126,6 +126,14 @@ def test_reduce_row_batches(nd):
     _reduce_case(psi, nd, nd // 2, wl.uniform_buckets(psi, 17_001), wl.Dist(0.05), 2000 + nd)
 
 
+@pytest.mark.parametrize("nd,bucket", [(1000, 3_001), (4096, 777)])
+def test_reduce_many_ranks(nd, bucket):
+    """Thousands of rows per bucket: the row loop, its batches and the 1/Nd scale."""
+    print(f"reduce nd={nd} bucket={bucket}", flush=True)
+    psi = nd * 2_003
+    _reduce_case(psi, nd, nd // 3, wl.uniform_buckets(psi, bucket), wl.Dist(1e-3), 3000 + nd)
+
+
 def test_reduce_special_values():
     """inf, NaN, fp16 subnormals, -0 and sums beyond the fp16 range, against the
     oracle (NaN compared as NaN, everything else bit for bit)."""
@@ -284,6 +292,36 @@ def test_adam_plain_dp_like_twenty_steps():
 
 def test_adam_heavy_tail_zero_moments():
     _adam_case(1_000_000, False, 5, 1e-4, 4244, wl.Dist(0.0), wl.Dist(0.0), heavy=True)
+
+
+@pytest.mark.parametrize("lr,b1,b2,eps,t", [
+    (1e-3, 0.0, 0.999, 1e-8, 1),        # no momentum
+    (1e-3, 0.9, 0.0, 1e-8, 2),          # no variance averaging
+    (0.0, 0.9, 0.999, 1e-8, 3),         # zero learning rate: the master stays
+    (1e-2, 0.9, 0.999, 1.0, 1),         # epsilon dominating the denominator
+    (1e-4, 0.9, 0.999, 1e-8, 10 ** 6),  # bias corrections at 1
+    (3e-4, 0.5, 0.75, 1e-6, 7),
+])
+def test_adam_hyperparameter_extremes(lr, b1, b2, eps, t):
+    n = 100_003
+    geom = Z.shard_geometry(n, 1, 0)
+    idx = np.arange(n, dtype=np.uint64)
+    th_h = gen.state_f32(77, gen.KIND_MASTER, idx, 0.02)
+    m_h = gen.state_f32(77, gen.KIND_M, idx, 1e-4)
+    v_h = gen.state_f32(77, gen.KIND_V, idx, 1e-6, True)
+    g_h = gen.grad_f16(77, 0, idx, 1e-3).view(np.float16).astype(np.float32)
+    th, m, v = (torch.from_numpy(a.copy()).cuda() for a in (th_h, m_h, v_h))
+    g = torch.from_numpy(g_h).cuda()
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    Z.adam_step_shard(geom, th, m, v, g, p, 0, lr, b1, b2, eps, t)
+    torch.cuda.synchronize()
+    sc = oadam.scalars(lr, b1, b2, eps, t)
+    want = oadam.step_values(th_h, m_h, v_h, g_h, sc)
+    assert_adam_step((th_h, m_h, v_h, g_h), (f32(th), f32(m), f32(v), u16(p)), want,
+                     c1=float(sc.c1), b1=float(sc.b1), b2=float(sc.b2), c2=float(sc.c2),
+                     what=f"lr={lr} b1={b1} b2={b2} eps={eps} t={t}")
+    if lr == 0.0:
+        assert_bits(f32(th), th_h, "master with lr = 0")
 
 
 def test_adam_special_values():
