@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle work to time on the host (seconds, approximate)")
     ap.add_argument("--check-samples", type=int, default=4096)
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the plain copy/fill rates reported for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (untimed) so that a counter "
                          "profile of this run holds a kernel of known traffic")
@@ -253,6 +255,8 @@ def main():
             parity.update(gather_check(w, geom, shards, layer_buf, init_idx, t_counter[0],
                                        stream))
 
+    ceilings = stream_ceilings(torch, dev, stream) if not args.no_ceilings else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, geom, args.cpu_chunk, args.cpu_seconds)
@@ -282,9 +286,37 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "ceilings": ceilings,
         "env": environment(torch, dev),
     }
     print(json.dumps(out), flush=True)
+
+
+def stream_ceilings(torch, dev, stream, nbytes=4 << 30, reps=10):
+    """Practical HBM rates of plain device operations on the same box, timed with HIP
+    events after the measurement: a device-to-device copy (nbytes read + nbytes
+    written) and a fill (nbytes written).  Context for the kernels' rates."""
+    n = nbytes // 4
+    with torch.cuda.stream(stream):
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("fill", lambda: dst.fill_(1.5), nbytes)):
+        with torch.cuda.stream(stream):
+            fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[f"{name}_gbs"] = moved / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def environment(torch, dev):
