@@ -1,0 +1,84 @@
+"""The path under HIP graph capture: one step (every bucket's reduce, then the
+Adam step with its fp16 slot write) is captured once and replayed; each replay,
+with eager work and synchronisations in between, must equal the same step run
+eagerly, bit for bit.  The entry points allocate nothing, never synchronise and
+use no memsets, so a caller can capture them (the scalars of the Adam step are
+fixed at capture, so every replay is a step with the same t)."""
+import numpy as np
+import pytest
+import torch
+
+import zero_sharded_mixed_bucketed_amd as Z
+from gpu_util import assert_bits, f32, need_gpu, rows_device, state_device, u16
+from synth import gen, workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    print(flush=True)
+
+
+def _setup(psi, nd, rank, bucket, seed):
+    geom = Z.shard_geometry(psi, nd, rank)
+    lo, n = geom.offset, geom.len
+    buckets = []
+    for off, blen in wl.buckets_touching(wl.uniform_buckets(psi, bucket), lo, lo + n):
+        a, b = Z.bucket_intersect(geom, off, blen)
+        buckets.append((a, b - a, rows_device(seed, nd, a, b - a, wl.Dist(1e-3))))
+    state = [state_device(seed, lo, n, wl.Dist(0.02), gen.KIND_MASTER),
+             state_device(seed, lo, n, wl.Dist(1e-4), gen.KIND_M),
+             state_device(seed, lo, n, wl.Dist(1e-6, True), gen.KIND_V)]
+    return geom, buckets, state
+
+
+@pytest.mark.parametrize("g16", [False, True])
+def test_captured_step_replays_equal_eager_steps(g16):
+    psi, nd, rank, bucket, seed, replays = 1_000_003, 8, 3, 100_003, 31, 4
+    geom, buckets, eager = _setup(psi, nd, rank, bucket, seed)
+    _, _, graphed = _setup(psi, nd, rank, bucket, seed)
+    dt = torch.int16 if g16 else torch.float32
+    g_e = torch.zeros(geom.len, dtype=dt, device="cuda")
+    g_g = torch.zeros(geom.len, dtype=dt, device="cuda")
+    p_e = torch.zeros(psi, dtype=torch.int16, device="cuda")
+    p_g = torch.zeros(psi, dtype=torch.int16, device="cuda")
+
+    def step(state, grad, flat16, stream=None):
+        for a, n, rows in buckets:
+            if g16:
+                Z.reduce_shard(geom, a, n, rows, None, grad, stream=stream)
+            else:
+                Z.reduce_shard(geom, a, n, rows, grad, stream=stream)
+        Z.adam_step_shard(geom, *state, grad, flat16, 0, 1e-4, 0.9, 0.999, 1e-8, 1,
+                          stream=stream)
+
+    # warm the library (device attributes) and the allocator before capture
+    scratch = [x.clone() for x in graphed]
+    step(scratch, g_g.clone(), p_g.clone())
+    torch.cuda.synchronize()
+    del scratch
+
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(graphed, g_g, p_g, stream=side)
+    torch.cuda.synchronize()
+    # capturing enqueues nothing: the state is still the initial one
+    assert_bits(f32(graphed[0]), f32(eager[0]), "state untouched by capture")
+
+    noise = torch.randn(1 << 20, device="cuda")
+    for r in range(replays):
+        step(eager, g_e, p_e)
+        graph.replay()
+        noise = noise * 1.0001 + 1.0          # eager work between replays
+        torch.cuda.synchronize()
+        for a, b, name in zip(graphed, eager, ("master", "m", "v")):
+            assert_bits(f32(a), f32(b), f"replay {r} {name}")
+        if g16:
+            assert_bits(u16(g_g), u16(g_e), f"replay {r} fp16 gradient shard")
+        else:
+            assert_bits(f32(g_g), f32(g_e), f"replay {r} gradient shard")
+        assert_bits(u16(p_g), u16(p_e), f"replay {r} fp16 vector")
+    assert np.isfinite(f32(noise)).all()
