@@ -9,6 +9,11 @@ at Nd = 64 (shard of 117,187,500 elements; 25M-element buckets, five of which
 meet the shard; fp16 gradients N(0, 1e-3); fp32 master N(0, 0.02), m N(0, 1e-4),
 v |N(0, 1e-6)|; lr 1e-4, betas 0.9/0.999, eps 1e-8).  The Nd ranks' local
 gradients of those buckets are synthetic and resident in HBM before timing.
+Other workloads (--workload): the same step with an fp16 gradient shard, stage
+3 with its per-layer parameter gathers, 13B at Nd = 32 with heavy-tailed
+gradients, 100B at Nd = 400 (rank 137; 200 GB of gradient rows resident,
+reduced in 2^22-column launches; the fp16 vector as a window around the slot),
+plain data parallelism at 1.4B, and a tiny case.
 
 Prints one JSON line: params/s of the whole step, HBM GB/s, per-kernel timings
 from HIP events on the launch stream, the roofline of the dominant kernel, a
@@ -38,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zero2-7.5B-nd64",
                     choices=["zero2-7.5B-nd64", "zero2-7.5B-nd64-g16", "zero3-7.5B-nd64",
-                             "zero2-13B-nd32", "plain-dp-1.4B", "tiny-zero2"])
+                             "zero2-13B-nd32", "zero2-100B-nd400", "plain-dp-1.4B",
+                             "tiny-zero2"])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunk", type=int, default=1 << 22,
@@ -64,6 +70,8 @@ def workload(name, rank):
         return wl.zero3_7p5b(0 if rank is None else rank)
     if name == "zero2-13B-nd32":
         return wl.zero2_13b(0 if rank is None else rank)
+    if name == "zero2-100B-nd400":
+        return wl.zero2_100b(137 if rank is None else rank)
     if name == "plain-dp-1.4B":
         return wl.plain_dp_1p4b()
     return wl.tiny()
@@ -114,9 +122,17 @@ def main():
                                         w.extra["param_sigma"], rank0=k, kind=gen.KIND_PARAM16)
             param16, param16_origin = shards[w.rank, :S], lo
             layer_buf = torch.empty(max(n for _, n in w.buckets), dtype=torch.int16, device=dev)
+        elif "p16_window" in w.extra:
+            # the rank's slot and a margin either side of it, at its place in the
+            # flat fp16 vector (the whole vector does not fit beside the rows)
+            win = w.extra["p16_window"]
+            param16_origin = max(0, lo - win)
+            param16 = torch.zeros(min(w.psi, lo + S + win) - param16_origin, dtype=torch.int16,
+                                  device=dev)
         else:
             param16, param16_origin = torch.zeros(w.psi, dtype=torch.int16, device=dev), 0
-        buckets = []          # (flat offset, length, rows) for the buckets meeting the shard
+        buckets = []          # (flat offset, length, rows) per reduce launch
+        n_buckets = 0         # buckets meeting the shard
         if w.fp16_grad:
             grad = torch.empty(S, dtype=torch.int16, device=dev)
             sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
@@ -124,13 +140,17 @@ def main():
         else:
             g16 = w.grad_shard == "fp16"
             grad = torch.zeros(S, dtype=torch.int16 if g16 else torch.float32, device=dev)
+            chunk = w.extra.get("chunk")          # rows arrive in column chunks
             for off, n in wl.buckets_touching(w.buckets, lo, lo + S):
                 a, b = Z.bucket_intersect(geom, off, n)
-                stride = (b - a + 63) // 64 * 64     # rows start on 128-byte cache lines
-                buf = torch.empty(w.nd * stride, dtype=torch.int16, device=dev)
-                rows = buf.as_strided((w.nd, b - a), (stride, 1))
-                sdev.fill_grad_rows(rows, w.seed, a, w.grad.sigma, w.grad.heavy_tail)
-                buckets.append((a, b - a, rows))
+                n_buckets += 1
+                for c0 in range(a, b, chunk or (b - a)):
+                    c1 = min(b, c0 + (chunk or (b - a)))
+                    stride = Z.row_stride(c1 - c0)
+                    buf = torch.empty(w.nd * stride, dtype=torch.int16, device=dev)
+                    rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
+                    sdev.fill_grad_rows(rows, w.seed, c0, w.grad.sigma, w.grad.heavy_tail)
+                    buckets.append((c0, c1 - c0, rows))
     torch.cuda.synchronize()
     init_idx = None
     if args.check_samples:
@@ -259,7 +279,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, geom, args.cpu_chunk, args.cpu_seconds)
+        # at most 2^28 fp16 gradient values per oracle chunk (512 MiB of host memory)
+        cpu_chunk = max(1 << 10, min(args.cpu_chunk, (1 << 28) // w.nd))
+        cpu = cpu_baseline(w, geom, cpu_chunk, args.cpu_seconds)
 
     step_bytes = sum(k["bytes_per_step"] for k in kernels.values())
     out = {
@@ -276,12 +298,17 @@ def main():
         "bytes_per_step": step_bytes,
         "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
                    "stage": 3 if stage3 else (1 if w.nd == 1 else 2),
-                   "shard_elements": S, "buckets_in_shard": len(buckets),
-                   "bucket_elements": wl.BUCKET if not stage3 else "layer",
+                   "shard_elements": S, "buckets_in_shard": n_buckets,
+                   "reduce_launches": len(buckets),
+                   "bucket_elements": ("layer" if stage3 else
+                                       max(n for _, n in w.buckets)),
+                   "chunk_elements": w.extra.get("chunk"),
                    "grad": "fp16 rows" if buckets else "fp16",
                    "grad_shard": ("fp32" if g_bytes == 4 else "fp16") if buckets else None,
                    "state": "fp32 master/m/v",
-                   "slot": "own fp16 shard" if stage3 else "fp16 flat vector"},
+                   "slot": ("own fp16 shard" if stage3 else
+                            "fp16 flat vector window" if "p16_window" in w.extra else
+                            "fp16 flat vector")},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

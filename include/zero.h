@@ -129,6 +129,21 @@ int zero_bucket_intersect(const zero_geom_t *g, uint64_t bucket_offset, uint64_t
                           uint64_t *lo, uint64_t *hi);
 
 /*
+ * Advised row stride, in elements, for the Nd fp16 gradient rows of a bucket
+ * (or chunk) of `len` columns that a caller lays out for zero_reduce_shard:
+ * len rounded up to a multiple of 64 elements (each row starts on a 128-byte
+ * line), plus 1024 elements when that stride is a whole number of MiB.  The
+ * reduce reads the Nd rows of a column tile at once, and on MI355X rows a power
+ * of two apart read slower: at Nd = 400, rows 4 or 8 MiB apart stream 12-14%
+ * slower than the same rows 2 KiB further apart, while on the other strides
+ * measured the pad changes nothing beyond run-to-run noise.  Advice only:
+ * zero_reduce_shard accepts any slice_stride >= bucket_len.  len == 0 gives 0.
+ * Errors: ZERO_E_INVAL (stride NULL), ZERO_E_RANGE (the stride would not fit in
+ * 64 bits).
+ */
+int zero_row_stride(uint64_t len, uint64_t *stride);
+
+/*
  * The owner's reduce of one gradient bucket (guide, "Como funciona": each
  * gradient is reduced only at the process that owns its partition, via
  * reduce-scatter, then released; card "ZeRO-2", "Gradient lifecycle").

@@ -169,7 +169,7 @@ def zero2_100b(rank: int = 137) -> Workload:
         name=f"zero2-100B-nd400-r{rank}", psi=psi, nd=400, rank=rank,
         buckets=tensor_buckets(psi, 8192), grad=Dist(1e-3), master=Dist(0.02),
         m=Dist(1e-4), v=Dist(1e-6, absolute=True), lr=1e-4, steps=5,
-        seed=_c(4), extra={"chunk": 1 << 22})
+        seed=_c(4), extra={"chunk": 1 << 22, "p16_window": 1 << 20})
 
 
 def buckets_touching(buckets, lo: int, hi: int):

@@ -54,6 +54,12 @@ int main() {
   EXPECT(zero_bucket_intersect(&g, 95, 10, &lo, &hi) == ZERO_E_RANGE);
   EXPECT(zero_bucket_intersect(&g, UINT64_MAX - 3, 10, &lo, &hi) == ZERO_E_RANGE);
   EXPECT(zero_bucket_intersect(NULL, 0, 1, &lo, &hi) == ZERO_E_INVAL);
+  uint64_t st = 0;
+  EXPECT(zero_row_stride(1ull << 22, &st) == ZERO_OK && st == (1ull << 22) + 1024);
+  EXPECT(zero_row_stride(UINT64_MAX - 1087, &st) == ZERO_OK && st % 64 == 0);
+  EXPECT(zero_row_stride(UINT64_MAX - 1086, &st) == ZERO_E_RANGE);
+  EXPECT(zero_row_stride(UINT64_MAX, &st) == ZERO_E_RANGE);
+  EXPECT(zero_row_stride(5, NULL) == ZERO_E_INVAL);
 
   // Adam scalars and their argument checks
   float sc[7];

@@ -34,6 +34,33 @@ def test_exports_every_declared_symbol():
         assert hasattr(Z.lib, name)
 
 
+def test_row_stride_rule():
+    """Rows start on 128-byte lines, and no stride is a whole number of MiB (such
+    strides get 2 KiB more); otherwise nothing is added."""
+    assert Z.row_stride(0) == 0
+    assert Z.row_stride(1) == 64
+    assert Z.row_stride(64) == 64
+    assert Z.row_stride(65) == 128
+    assert Z.row_stride(25_000_000) == 25_000_000
+    assert Z.row_stride(17_187_500) == 17_187_520
+    assert Z.row_stride(1 << 22) == (1 << 22) + 1024           # 8 MiB rows
+    assert Z.row_stride((1 << 22) - 5) == (1 << 22) + 1024
+    assert Z.row_stride(1 << 19) == (1 << 19) + 1024           # 1 MiB rows
+    assert Z.row_stride(3 << 19) == (3 << 19) + 1024           # 3 MiB rows
+    assert Z.row_stride((1 << 19) + 1) == (1 << 19) + 64
+    rng = np.random.default_rng(5)
+    for n in list(rng.integers(1, 1 << 40, size=2000)) + [k << 19 for k in range(1, 300)]:
+        n = int(n)
+        s = Z.row_stride(n)
+        assert s >= n and s % 64 == 0 and (s * 2) % (1 << 20) != 0
+        assert s - n < 64 + 1024
+        if ((n + 63) // 64 * 64 * 2) % (1 << 20):
+            assert s == (n + 63) // 64 * 64
+    with pytest.raises(Z.ZeroError):
+        Z.row_stride((1 << 64) - 1)
+    assert Z.row_stride((1 << 64) - 1088) % 64 == 0
+
+
 def test_memory_model_matches_oracle_and_print():
     for psi in (1 << 20, 1_400_000_000, 7_500_000_000, 13_000_000_000, 10 ** 11):
         for nd in (1, 4, 32, 64, 400):

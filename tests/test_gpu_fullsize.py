@@ -49,7 +49,7 @@ def _host_state(w, flat):
 
 def _reduce_all(w, geom, grad32, chunk=None):
     """Every bucket that meets the shard, in arrival order; only the owned columns
-    arrive (row stride padded to 64 elements); the rows are freed after each call."""
+    arrive (rows at the library's advised stride); the rows are freed after each call."""
     edges = []
     for off, n in wl.buckets_touching(w.buckets, geom.offset, geom.offset + geom.len):
         a, b = Z.bucket_intersect(geom, off, n)
@@ -57,7 +57,7 @@ def _reduce_all(w, geom, grad32, chunk=None):
         step = chunk or (b - a)
         for c0 in range(a, b, step):
             c1 = min(b, c0 + step)
-            stride = (c1 - c0 + 63) // 64 * 64
+            stride = Z.row_stride(c1 - c0)
             buf = torch.empty(w.nd * stride, dtype=torch.int16, device="cuda")
             rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
             sdev.fill_grad_rows(rows, w.seed, c0, w.grad.sigma, w.grad.heavy_tail)
@@ -131,7 +131,7 @@ def test_fullsize_zero2_100b_rank137():
     """100B at Nd = 400, rank 137: 11 tensor-sized buckets, 400 rows streamed in 2^22-element
     chunks, fp16 vector as a window around the slot, 5 steps."""
     w = wl.zero2_100b(137)
-    _run_zero2(w, chunk=w.extra["chunk"], window=1 << 20)
+    _run_zero2(w, chunk=w.extra["chunk"], window=w.extra["p16_window"])
 
 
 def test_fullsize_plain_dp_1p4b():
@@ -167,7 +167,7 @@ def test_fullsize_zero2_13b_probe():
     p_lo, p_hi = geom1.offset - probe // 2, geom1.offset + probe // 2
     for off, n in wl.buckets_touching(w1.buckets, geom1.offset, p_hi):
         a, b = Z.bucket_intersect(geom1, off, n)
-        stride = (b - a + 63) // 64 * 64
+        stride = Z.row_stride(b - a)
         buf = torch.empty(w1.nd * stride, dtype=torch.int16, device="cuda")
         rows = buf.as_strided((w1.nd, b - a), (stride, 1))
         sdev.fill_grad_rows(rows, w1.seed, a, w1.grad.sigma, w1.grad.heavy_tail)

@@ -38,7 +38,7 @@ STAGE_DP, STAGE_OS, STAGE_OS_G, STAGE_OS_G_P = 0, 1, 2, 3
 
 # Symbols that include/zero.h declares.
 EXPORTS = ("zero_memory_model", "zero_memory_model_k", "zero_comm_volume",
-           "zero_shard_geometry", "zero_bucket_intersect",
+           "zero_shard_geometry", "zero_bucket_intersect", "zero_row_stride",
            "zero_reduce_shard", "zero_adam_scalars", "zero_adam_step_shard",
            "zero_gather_params", "zero_last_error")
 
@@ -106,6 +106,8 @@ def _load() -> ctypes.CDLL:
     lib.zero_shard_geometry.restype = ci
     lib.zero_bucket_intersect.argtypes = [G, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(u64)]
     lib.zero_bucket_intersect.restype = ci
+    lib.zero_row_stride.argtypes = [u64, ctypes.POINTER(u64)]
+    lib.zero_row_stride.restype = ci
     lib.zero_reduce_shard.argtypes = [G, u64, u64, vp, u64, vp, vp, vp]
     lib.zero_reduce_shard.restype = ci
     lib.zero_adam_scalars.argtypes = [dbl, dbl, dbl, dbl, u64, ctypes.POINTER(ctypes.c_float)]
@@ -165,6 +167,13 @@ def bucket_intersect(geom: Geom, offset: int, length: int) -> Tuple[int, int]:
     _check(lib.zero_bucket_intersect(ctypes.byref(geom), offset, length, ctypes.byref(lo),
                                      ctypes.byref(hi)))
     return lo.value, hi.value
+
+
+def row_stride(length: int) -> int:
+    """Advised stride (elements) between the Nd gradient rows of `length` columns."""
+    out = ctypes.c_uint64()
+    _check(lib.zero_row_stride(length, ctypes.byref(out)))
+    return out.value
 
 
 def adam_scalars(lr: float, beta1: float, beta2: float, eps: float, step: int):

@@ -190,6 +190,17 @@ int zero_bucket_intersect(const zero_geom_t* g, uint64_t bucket_offset, uint64_t
   return ok();
 }
 
+int zero_row_stride(uint64_t len, uint64_t* stride) {
+  if (!stride) return fail(ZERO_E_INVAL, "stride is NULL");
+  constexpr uint64_t kLine = 64, kPad = 1024, kMiBElems = (1u << 20) / 2;
+  if (len > UINT64_MAX - (kLine - 1) - kPad)
+    return fail(ZERO_E_RANGE, "len %llu too large", (unsigned long long)len);
+  uint64_t s = (len + kLine - 1) / kLine * kLine;
+  if (s != 0 && s % kMiBElems == 0) s += kPad;
+  *stride = s;
+  return ok();
+}
+
 int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t bucket_len,
                       const uint16_t* slices, uint64_t slice_stride, float* grad32,
                       uint16_t* grad16, void* hip_stream) {
