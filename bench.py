@@ -53,7 +53,7 @@ def parse():
                     help="oracle work to time on the host (seconds, approximate)")
     ap.add_argument("--check-samples", type=int, default=4096)
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the plain copy/fill rates reported for context")
+                    help="skip the streaming ceilings reported for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (untimed) so that a counter "
                          "profile of this run holds a kernel of known traffic")
@@ -235,6 +235,7 @@ def main():
     for k in range(args.steps):
         ops = step(per_step[k])
     end.record(stream)
+    enqueued = time.perf_counter() - wall0         # host time to issue the timed steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
@@ -275,7 +276,13 @@ def main():
             parity.update(gather_check(w, geom, shards, layer_buf, init_idx, t_counter[0],
                                        stream))
 
-    ceilings = stream_ceilings(torch, dev, stream) if not args.no_ceilings else None
+    ceilings = None
+    if not args.no_ceilings:
+        widest = max((n for _, n, _ in buckets), default=None)
+        ceilings = stream_ceilings(torch, dev, stream,
+                                   (w.nd, widest) if widest else None)
+        if "reduce" in kernels and "read_rows_gbs" in ceilings:
+            ceilings["reduce_of_read_rows"] = kernels["reduce"]["gbs"] / ceilings["read_rows_gbs"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -291,6 +298,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "hbm_gbs": gbs(step_bytes, ms_step),
@@ -319,18 +327,21 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def stream_ceilings(torch, dev, stream, nbytes=4 << 30, reps=10):
-    """Practical HBM rates of plain device operations on the same box, timed with HIP
-    events after the measurement: a device-to-device copy (nbytes read + nbytes
-    written) and a fill (nbytes written).  Context for the kernels' rates."""
-    n = nbytes // 4
-    with torch.cuda.stream(stream):
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    out = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
-                            ("fill", lambda: dst.fill_(1.5), nbytes)):
+def stream_ceilings(torch, dev, stream, rows_shape=None, nbytes=4 << 30, reps=10):
+    """Practical HBM rates on the same box, timed with HIP events on the launch
+    stream after the measurement; context for the kernels' rates.
+
+    - read_rows: the reduce's access pattern over Nd rows of the workload's widest
+      launch (at most nbytes of rows), without its arithmetic and stores, at the
+      reduce's occupancy cap;
+    - write, copy: 16-byte stores / non-temporal loads and stores over nbytes,
+      no occupancy cap;
+    - runtime_copy, runtime_fill: torch's own device copy_ and fill_ over nbytes.
+    """
+    import zero_sharded_mixed_bucketed_amd as Z
+    from synth import probe
+
+    def timed(fn):
         with torch.cuda.stream(stream):
             fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -339,8 +350,33 @@ def stream_ceilings(torch, dev, stream, nbytes=4 << 30, reps=10):
                 fn()
             b.record(stream)
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        out[f"{name}_gbs"] = moved / (ms * 1e-3) / 1e9
+        return a.elapsed_time(b) / reps
+
+    gbs = lambda moved, ms: moved / (ms * 1e-3) / 1e9
+    out = {}
+    if rows_shape is not None:
+        nd, cols = rows_shape
+        cols = min(cols, nbytes // (2 * nd)) // 8 * 8
+        stride = Z.row_stride(cols)
+        with torch.cuda.stream(stream):
+            buf = torch.ones(nd * stride, dtype=torch.int16, device=dev)
+            sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        rows = buf.as_strided((nd, cols), (stride, 1))
+        ms = timed(lambda: probe.read_rows(rows, sink, 8, stream=stream))
+        out["read_rows_gbs"] = gbs(2 * nd * cols, ms)
+        out["read_rows_shape"] = [nd, cols, stride]
+        del rows, buf, sink
+    n = nbytes // 4
+    with torch.cuda.stream(stream):
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for name, fn, moved in (("write", lambda c: probe.write(dst, c, stream=stream), nbytes),
+                            ("copy", lambda c: probe.copy(src, dst, c, stream=stream),
+                             2 * nbytes)):
+        out[f"{name}_gbs"] = gbs(moved, timed(lambda: fn(0)))
+    out["runtime_copy_gbs"] = gbs(2 * nbytes, timed(lambda: dst.copy_(src)))
+    out["runtime_fill_gbs"] = gbs(nbytes, timed(lambda: dst.fill_(1.5)))
     del src, dst
     torch.cuda.empty_cache()
     return out
