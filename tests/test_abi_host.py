@@ -266,3 +266,18 @@ def test_gather_rejects(call, code):
 def test_gather_empty_is_ok_without_device():
     assert _gather(n=0, shards=None, out=None) == Z.ZERO_OK
     assert _gather(lo=100, n=0) == Z.ZERO_OK
+
+
+def test_c_consumer_links_and_rejects_bad_input(tmp_path):
+    """The plain C consumer of the library starts (its libzero.so and HIP runtime
+    resolve) and refuses a bad command line or a short input before any device
+    call."""
+    exe = os.path.join(ROOT, "tests", "native", "build", "abi_gpu_driver")
+    assert os.path.exists(exe), "not built; run __graft_entry__.build()"
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=30)
+    assert r.returncode == 2 and "usage" in r.stderr
+    short = tmp_path / "short.bin"
+    short.write_bytes(b"\x00" * 10)
+    r = subprocess.run([exe, str(short), str(tmp_path / "out.bin")], capture_output=True,
+                       text=True, timeout=30)
+    assert r.returncode == 2 and "short input" in r.stderr
