@@ -175,8 +175,11 @@ int zero_row_stride(uint64_t len, uint64_t *stride);
  * The "release" of the rest of the local gradient is the caller freeing
  * `slices` after this call completes on the stream.  An empty intersection is
  * ZERO_OK and enqueues nothing.
+ * Nd is at most 2^24 here (the largest Nd for which RN32(1/Nd) is the fp32
+ * quotient 1 / fp32(Nd)).
  * Errors: ZERO_E_INVAL (slices NULL, both outputs NULL, bad geometry),
- * ZERO_E_RANGE (bucket beyond psi, slice_stride < bucket_len, size overflow),
+ * ZERO_E_RANGE (bucket beyond psi, slice_stride < bucket_len, size overflow,
+ * Nd > 2^24 for a bucket that meets the shard),
  * ZERO_E_ALIGN (slices or grad16 not 2-byte, grad32 not 4-byte aligned),
  * ZERO_E_DEVICE (launch failed).
  */

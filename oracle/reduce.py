@@ -41,8 +41,14 @@ import numpy as np
 from . import geometry
 
 
+MAX_ND = 1 << 24
+
+
 def inv_nd(nd: int) -> np.float32:
-    """RN32(1 / Nd): IEEE single division is correctly rounded."""
+    """RN32(1 / Nd): IEEE single division is correctly rounded, and fp32(Nd) is
+    Nd itself for Nd <= 2^24; larger Nd are refused."""
+    if not 1 <= nd <= MAX_ND:
+        raise ValueError(f"Nd must lie in [1, 2^24], got {nd}")
     return np.float32(1.0) / np.float32(nd)
 
 

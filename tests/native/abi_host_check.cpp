@@ -82,6 +82,11 @@ int main() {
   EXPECT(zero_reduce_shard(&g, 25, 25, fake16 + 0, 25, (float*)((char*)fake32 + 2), NULL,
                            NULL) == ZERO_E_ALIGN);
   EXPECT(zero_reduce_shard(&g, 0, 10, NULL, 0, NULL, NULL, NULL) == ZERO_OK);   // misses the shard
+  {
+    zero_geom_t big;
+    EXPECT(zero_shard_geometry(1ull << 30, (1u << 24) + 1, 0, &big) == ZERO_OK);
+    EXPECT(zero_reduce_shard(&big, 0, 10, fake16, 10, fake32, NULL, NULL) == ZERO_E_RANGE);
+  }
   zero_geom_t bad = g;
   bad.offset += 1;
   EXPECT(zero_reduce_shard(&bad, 25, 25, fake16, 25, fake32, NULL, NULL) == ZERO_E_INVAL);

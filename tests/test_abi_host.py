@@ -182,6 +182,9 @@ def _reduce(g, off=25, n=25, slices=FAKE, stride=25, g32=FAKE, g16=None):
     (lambda: _reduce(_geom(), slices=FAKE + 1), Z.ZERO_E_ALIGN),
     (lambda: _reduce(_geom(), g32=FAKE + 2), Z.ZERO_E_ALIGN),
     (lambda: _reduce(_geom(), g16=FAKE + 1), Z.ZERO_E_ALIGN),
+    # Nd above 2^24, where fp32(Nd) is no longer Nd, for a bucket that meets the shard
+    (lambda: _reduce(_geom(psi=1 << 30, nd=(1 << 24) + 1, rank=0), off=0, n=10),
+     Z.ZERO_E_RANGE),
 ])
 def test_reduce_rejects(call, code):
     assert call() == code

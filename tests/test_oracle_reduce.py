@@ -61,6 +61,31 @@ def test_hand_worked_cases(golden_dir):
         assert hex(int(g16[0])) == hex(int(c["grad16"], 16)), c["name"]
 
 
+def _rn32_of_reciprocal(nd):
+    """The fp32 value nearest 1/nd by exact rational comparison (ties to even)."""
+    from fractions import Fraction
+    exact = Fraction(1, nd)
+    f = np.float32(1.0 / nd)
+    cands = [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(1))]
+    best = min(abs(Fraction(float(c)) - exact) for c in cands)
+    near = [c for c in cands if abs(Fraction(float(c)) - exact) == best]
+    return min(near, key=lambda c: int(c.view(np.uint32)) & 1)
+
+
+def test_inv_nd_is_the_correctly_rounded_reciprocal():
+    rng = np.random.default_rng(24)
+    nds = [1, 2, 3, 7, 64, 400, 1000, 4096, 12345, (1 << 24) - 1, 1 << 24] + \
+        [int(x) for x in rng.integers(1, 1 << 24, size=3000)]
+    for nd in nds:
+        assert red.inv_nd(nd).view(np.uint32) == _rn32_of_reciprocal(nd).view(np.uint32), nd
+
+
+@pytest.mark.parametrize("nd", [0, (1 << 24) + 1, 1 << 30])
+def test_inv_nd_refuses_nd_outside_the_exact_range(nd):
+    with pytest.raises(ValueError):
+        red.inv_nd(nd)
+
+
 def test_nd1_is_identity():
     rows = gen.grad_rows(5, 1, 0, 10000, 0.3)
     got = red.reduce_values(rows, 1)

@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
     float r[kCols];
 #pragma unroll
     for (int e = 0; e < kCols; ++e) r[e] = acc[e] * a.inv;
-    store_full(a, static_cast<uint64_t>(static_cast<int64_t>(c) + a.delta), r);
+    store_full(a, c + static_cast<uint64_t>(a.delta), r);
     return;
   }
 
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
     const uint64_t col = c + e;
     if (col >= a.c_lo && col < a.c_hi) {
       const float r = acc[e] * a.inv;
-      const uint64_t o = static_cast<uint64_t>(static_cast<int64_t>(col) + a.delta);
+      const uint64_t o = col + static_cast<uint64_t>(a.delta);
       if (a.out32) a.out32[o] = r;
       if (a.out16) a.out16[o] = static_cast<uint16_t>(f2h(r));
     }
@@ -230,7 +230,7 @@ hipError_t launch_reduce(const ReduceLaunch& L, const DeviceInfo& d, hipStream_t
   const int w = static_cast<int>(ra & (~ra + 1));   // lowest set bit, at most 16
   // Alignment of the output addresses of full groups: column col0 + 8j maps to
   // out32 + col0 + delta + 8j, so the alignment class is the same for all.
-  const uint64_t o0 = static_cast<uint64_t>(static_cast<int64_t>(a.col0) + a.delta);
+  const uint64_t o0 = a.col0 + static_cast<uint64_t>(a.delta);
   a.st32 = 1;
   if (L.out32) {
     const uintptr_t b32 = reinterpret_cast<uintptr_t>(L.out32) + 4 * o0;

@@ -15,6 +15,8 @@ namespace {
 
 thread_local char g_err[512];
 
+constexpr uint32_t kMaxReduceNd = 1u << 24;
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -211,6 +213,9 @@ int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t buc
   const uint64_t a = bucket_offset > s_lo ? bucket_offset : s_lo;
   const uint64_t b = (bucket_offset + bucket_len) < s_hi ? (bucket_offset + bucket_len) : s_hi;
   if (a >= b) return ok();  // nothing of this bucket is owned here
+  // RN32(1/Nd) is 1.0f / float(Nd) only while Nd is exact in fp32
+  if (g->nd > kMaxReduceNd)
+    return fail(ZERO_E_RANGE, "nd %u exceeds the reduce's limit of 2^24 ranks", g->nd);
   if (!slices) return fail(ZERO_E_INVAL, "slices must not be NULL");
   if (!grad32 && !grad16) return fail(ZERO_E_INVAL, "grad32 and grad16 are both NULL");
   if (slice_stride < bucket_len)
@@ -228,8 +233,9 @@ int zero_reduce_shard(const zero_geom_t* g, uint64_t bucket_offset, uint64_t buc
   L.nd = g->nd;
   L.c_lo = a - bucket_offset;
   L.c_hi = b - bucket_offset;
-  // output index of column c is (bucket_offset + c) - shard offset
-  L.delta = static_cast<int64_t>(bucket_offset) - static_cast<int64_t>(s_lo);
+  // output index of column c is (bucket_offset + c) - shard offset; the
+  // difference is taken modulo 2^64 and read back as a signed shift
+  L.delta = static_cast<int64_t>(bucket_offset - s_lo);
   L.out32 = grad32;
   L.out16 = grad16;
   L.inv_nd = 1.0f / static_cast<float>(g->nd);
