@@ -284,3 +284,17 @@ def test_c_consumer_links_and_rejects_bad_input(tmp_path):
     r = subprocess.run([exe, str(short), str(tmp_path / "out.bin")], capture_output=True,
                        text=True, timeout=30)
     assert r.returncode == 2 and "short input" in r.stderr
+
+
+def test_binding_requires_one_device_per_call():
+    """Every tensor of a call and its stream must share one device (checked on
+    stand-ins; the library launches on that device)."""
+    from types import SimpleNamespace as NS
+    import torch
+    a, b = torch.device("cuda", 0), torch.device("cuda", 1)
+    assert Z._one_device([NS(device=a), NS(device=a)], None) == a
+    assert Z._one_device([NS(device=a)], NS(device=a)) == a
+    with pytest.raises(ValueError):
+        Z._one_device([NS(device=a), NS(device=b)], None)
+    with pytest.raises(ValueError):
+        Z._one_device([NS(device=a)], NS(device=b))

@@ -183,10 +183,30 @@ def adam_scalars(lr: float, beta1: float, beta2: float, eps: float, step: int):
     return tuple(out)
 
 
-def _stream_handle(stream) -> ctypes.c_void_p:
+def _one_device(tensors, stream):
+    """The one device every tensor of a call (and the stream, if given) is on."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"tensors of one call are on {dev} and {t.device}")
+    if stream is not None and stream.device != dev:
+        raise ValueError(f"the stream is on {stream.device}, the tensors on {dev}")
+    return dev
+
+
+def _launch(tensors, stream, call) -> None:
+    """Runs call(stream_handle) with the tensors' device current: the library
+    launches on the current device, on the given stream (default: that
+    device's current stream)."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    dev = _one_device([t for t in tensors if t is not None], stream)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    handle = ctypes.c_void_p(s.cuda_stream)
+    if torch.cuda.current_device() == dev.index:
+        _check(call(handle))
+    else:
+        with torch.cuda.device(dev):
+            _check(call(handle))
 
 
 def _dev(t, name, dtypes, numel_at_least=None):
@@ -224,11 +244,10 @@ def reduce_shard(geom: Geom, bucket_offset: int, bucket_len: int, slices, grad32
         _dev(grad16, "grad16", f16, geom.len)
         if not grad16.is_contiguous():
             raise ValueError("grad16 must be contiguous")
-    _check(lib.zero_reduce_shard(ctypes.byref(geom), bucket_offset, bucket_len,
-                                 slices.data_ptr(), slices.stride(0),
-                                 grad32.data_ptr() if grad32 is not None else None,
-                                 grad16.data_ptr() if grad16 is not None else None,
-                                 _stream_handle(stream)))
+    _launch((slices, grad32, grad16), stream, lambda h: lib.zero_reduce_shard(
+        ctypes.byref(geom), bucket_offset, bucket_len, slices.data_ptr(), slices.stride(0),
+        grad32.data_ptr() if grad32 is not None else None,
+        grad16.data_ptr() if grad16 is not None else None, h))
 
 
 def adam_step_shard(geom: Geom, master, m, v, grad, param16: Optional[object],
@@ -259,8 +278,8 @@ def adam_step_shard(geom: Geom, master, m, v, grad, param16: Optional[object],
         s.param16 = param16.data_ptr()
         s.param16_origin = param16_origin
         s.param16_len = param16.numel()
-    _check(lib.zero_adam_step_shard(ctypes.byref(geom), ctypes.byref(s), lr, beta1, beta2, eps,
-                                    step, _stream_handle(stream)))
+    _launch((master, m, v, grad, param16), stream, lambda h: lib.zero_adam_step_shard(
+        ctypes.byref(geom), ctypes.byref(s), lr, beta1, beta2, eps, step, h))
 
 
 def gather_params(psi: int, nd: int, lo: int, length: int, shards, out, stream=None) -> None:
@@ -277,5 +296,5 @@ def gather_params(psi: int, nd: int, lo: int, length: int, shards, out, stream=N
     _dev(out, "out", f16, length)
     if not out.is_contiguous():
         raise ValueError("out must be contiguous")
-    _check(lib.zero_gather_params(psi, nd, lo, length, shards.data_ptr(), shards.stride(0),
-                                  out.data_ptr(), _stream_handle(stream)))
+    _launch((shards, out), stream, lambda h: lib.zero_gather_params(
+        psi, nd, lo, length, shards.data_ptr(), shards.stride(0), out.data_ptr(), h))
