@@ -591,13 +591,13 @@ def _oracle_chunk_timed(args):
     return os.getpid(), n, t_red + t_adam
 
 
-def cpu_baseline_all_cores(w, geom, chunk, rounds=2):
+def cpu_baseline_all_cores(w, geom, chunk, chunks_per_worker=2):
     """The same unchanged oracle over chunks in one process per host core (the work
     is element-wise, so chunks are independent): elements over the busiest worker's
-    oracle time.  Each worker takes about `rounds` chunks."""
+    oracle time.  Each worker takes about `chunks_per_worker` chunks."""
     import multiprocessing as mp
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    n_chunks = min(workers * rounds, -(-geom.len // chunk))
+    n_chunks = min(workers * chunks_per_worker, -(-geom.len // chunk))
     jobs = [(w, geom.offset + i * chunk, min(chunk, geom.len - i * chunk)) for i in range(n_chunks)]
     with mp.get_context("fork").Pool(workers) as pool:
         res = pool.map(_oracle_chunk_timed, jobs, chunksize=1)
