@@ -264,7 +264,8 @@ def main():
         kernels[kind] = {
             "kernel": names[kind], "launches_per_step": len(idx),
             "avg_ms_per_launch": avg_step / len(idx), "avg_ms_per_step": avg_step,
-            "min_ms_per_step": min(per), "bytes_per_step": bytes_step,
+            "min_ms_per_step": min(per), "median_ms_per_step": float(np.median(per)),
+            "bytes_per_step": bytes_step,
             "bytes_per_element": bytes_step / S,
             "gbs": gbs(bytes_step, avg_step), "frac_of_peak": gbs(bytes_step, avg_step) / PEAK_HBM_GBS,
             "params_per_s": S / (avg_step * 1e-3)}
