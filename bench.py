@@ -414,11 +414,12 @@ def kernel_source_sha256(kernel):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel, workload_name):
+def measured_traffic(kernel, workload_name, profiles_dir=None):
     """HBM bytes per launch from the committed counter summary of this kernel and
     workload, or None when there is none or the kernel source changed since."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", f"{kernel}__{workload_name}.md")
+    path = os.path.join(profiles_dir or os.path.join(here, "profiles"),
+                        f"{kernel}__{workload_name}.md")
     if not os.path.exists(path):
         return None
     fields = {}

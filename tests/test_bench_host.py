@@ -1,0 +1,84 @@
+"""bench.py's host logic on the CPU (no GPU needed): it refuses more than one GPU,
+every workload choice maps to a workload, the counter summaries it reads for
+roofline.traffic are looked up by kernel and workload and ignored once the kernel
+source has changed, and every committed summary carries the fields it reads and a
+command that runs committed files only."""
+import hashlib
+import importlib.util
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_refuses_more_than_one_gpu(argv, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT,
+                       env=dict(os.environ, **env))
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr and r.stdout == ""
+
+
+def test_every_workload_choice_maps_to_a_workload():
+    b = _bench()
+    names = {"zero2-7.5B-nd64": "zero2-7.5B-nd64-r0", "zero2-7.5B-nd64-g16": "zero2-7.5B-nd64-g16-r0",
+             "zero3-7.5B-nd64": "zero3-7.5B-nd64-r0", "zero2-13B-nd32": "zero2-13B-nd32-r0",
+             "zero2-100B-nd400": "zero2-100B-nd400-r137", "plain-dp-1.4B": "plain-dp-psi1400000000"}
+    for arg, name in names.items():
+        assert b.workload(arg, None).name == name
+    assert b.workload("zero2-7.5B-nd64", 3).rank == 3
+    assert b.workload("tiny-zero2", None).psi == 1 << 20
+
+
+def _summary(dirpath, kernel, workload, sha, nbytes):
+    path = os.path.join(dirpath, f"{kernel}__{workload}.md")
+    with open(path, "w") as f:
+        f.write(f"# {kernel} -- {workload}\n\n- measured HBM bytes per launch: {nbytes}\n"
+                f"- kernel source sha256: `{sha}`\n")
+
+
+def test_traffic_lookup_rules(tmp_path):
+    b = _bench()
+    sha = b.kernel_source_sha256("reduce_kernel")
+    d = str(tmp_path)
+    assert b.measured_traffic("reduce_kernel", "w1", d) is None           # no summary
+    _summary(d, "reduce_kernel", "w1", sha, 123456)
+    assert b.measured_traffic("reduce_kernel", "w1", d) == 123456
+    _summary(d, "reduce_kernel", "w2", "0" * 64, 123456)                 # source changed since
+    assert b.measured_traffic("reduce_kernel", "w2", d) is None
+    _summary(d, "adam_vec_kernel", "w1", sha, 99)                        # another kernel's source
+    assert b.measured_traffic("adam_vec_kernel", "w1", d) is None
+    assert sha == hashlib.sha256(open(os.path.join(
+        ROOT, "zero_sharded_mixed_bucketed_amd", "csrc", "reduce_shard.hip"), "rb").read()).hexdigest()
+
+
+def test_committed_summaries_are_well_formed():
+    b = _bench()
+    pdir = os.path.join(ROOT, "profiles")
+    files = [f for f in os.listdir(pdir) if f.endswith(".md")]
+    assert files
+    r = subprocess.run(["git", "ls-files"], cwd=ROOT, capture_output=True, text=True)
+    if r.returncode == 0:
+        tracked = set(r.stdout.split())
+    else:                                  # a copy of the tree without its history
+        tracked = {p for p in ("bench.py",) if os.path.exists(os.path.join(ROOT, p))}
+    for f in files:
+        kernel, workload = f[:-3].split("__")
+        assert kernel in b.KERNEL_SOURCES, f
+        text = open(os.path.join(pdir, f)).read()
+        assert re.search(r"^- measured HBM bytes per launch: \d+$", text, re.M), f
+        assert re.search(r"^- kernel source sha256: `[0-9a-f]{64}`$", text, re.M), f
+        cmds = re.findall(r"rocprofv3 .* -- python3 (\S+)", text)
+        assert cmds and all(c in tracked for c in cmds), (f, cmds)
