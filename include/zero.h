@@ -29,10 +29,15 @@
  *    stream) and the call returns at once; results are valid after the stream
  *    synchronises.  Calls that touch the same buffers must be ordered by the
  *    caller (same stream or events).
+ *  - Kernels run on the calling thread's current HIP device; every device
+ *    pointer of a call must be memory of that device.
  *  - A negative status is an error.  Arguments are validated before any HIP
  *    call, so a rejected call enqueues nothing and writes nothing.
  *    zero_last_error() returns a message for the calling thread's last error.
  *    Non-finite values in the data are not errors; they propagate per IEEE.
+ *  - Several threads may call at once.  The only process-wide state is a cache
+ *    of each device's compute-unit count and LDS size, filled atomically on
+ *    first use; the error message is per thread.
  */
 #ifndef ZERO_H_
 #define ZERO_H_
