@@ -298,3 +298,28 @@ def test_binding_requires_one_device_per_call():
         Z._one_device([NS(device=a), NS(device=b)], None)
     with pytest.raises(ValueError):
         Z._one_device([NS(device=a)], NS(device=b))
+
+
+def test_last_error_is_per_thread():
+    """Concurrent failing calls (ctypes drops the GIL around them): each thread
+    reads back the message of its own last error."""
+    import threading
+    errors = []
+
+    def worker(i):
+        g = _geom()
+        for _ in range(2000):
+            # stride 24 + i < bucket length 25 + i: the message names both values
+            rc = Z.lib.zero_reduce_shard(ctypes.byref(g), 25, 25, FAKE, 24 - (i % 20), FAKE,
+                                         None, None)
+            msg = Z.last_error()
+            if rc != Z.ZERO_E_RANGE or f"slice_stride {24 - (i % 20)} " not in msg:
+                errors.append((i, rc, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
