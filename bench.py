@@ -25,6 +25,7 @@ the host as a baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -46,6 +47,8 @@ def parse():
                              "zero2-13B-nd32", "zero2-100B-nd400", "plain-dp-1.4B",
                              "tiny-zero2"])
     ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunk", type=int, default=1 << 22,
                     help="shard elements per chunk of the oracle's timed sample")
@@ -92,6 +95,8 @@ def main():
     from synth import workloads as wl
 
     w = workload(args.workload, args.rank)
+    if args.seed is not None:
+        w = dataclasses.replace(w, seed=args.seed)
     stage3 = w.extra.get("stage") == 3
     geom = Z.shard_geometry(w.psi, w.nd, w.rank)
     S, lo = geom.len, geom.offset
@@ -317,6 +322,7 @@ def main():
         "hbm_frac_of_peak": gbs(step_bytes, ms_step) / PEAK_HBM_GBS,
         "bytes_per_step": step_bytes,
         "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
+                   "seed": w.seed,
                    "stage": 3 if stage3 else (1 if w.nd == 1 else 2),
                    "shard_elements": S, "buckets_in_shard": n_buckets,
                    "reduce_launches": len(buckets),
@@ -400,7 +406,23 @@ def environment(torch, dev):
     return {"device": p.name, "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
             "hip": torch.version.hip, "torch": torch.__version__,
-            "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0))}
+            "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0)),
+            "library_sources_sha256": library_sources_sha256()}
+
+
+def library_sources_sha256():
+    """One digest over the library's header and HIP sources: which build ran."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    paths = []
+    for d in (os.path.join(here, "include"),
+              os.path.join(here, "zero_sharded_mixed_bucketed_amd", "csrc")):
+        paths += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".h", ".hip"))]
+    for path in paths:
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 KERNEL_SOURCES = {"reduce_kernel": "reduce_shard.hip", "adam_vec_kernel": "adam_step_shard.hip",

@@ -82,3 +82,17 @@ def test_committed_summaries_are_well_formed():
         assert re.search(r"^- kernel source sha256: `[0-9a-f]{64}`$", text, re.M), f
         cmds = re.findall(r"rocprofv3 .* -- python3 (\S+)", text)
         assert cmds and all(c in tracked for c in cmds), (f, cmds)
+
+
+def test_library_sources_digest_tracks_the_sources(tmp_path):
+    b = _bench()
+    d1 = b.library_sources_sha256()
+    assert d1 == b.library_sources_sha256() and len(d1) == 64
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("zero_sharded_mixed_bucketed_amd", "csrc")):
+        d = os.path.join(ROOT, sub)
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".h", ".hip")):
+                h.update(f.encode())
+                h.update(open(os.path.join(d, f), "rb").read())
+    assert d1 == h.hexdigest()
