@@ -82,3 +82,62 @@ def test_captured_step_replays_equal_eager_steps(g16):
             assert_bits(f32(g_g), f32(g_e), f"replay {r} gradient shard")
         assert_bits(u16(p_g), u16(p_e), f"replay {r} fp16 vector")
     assert np.isfinite(f32(noise)).all()
+
+
+def test_captured_stage3_step_replays_equal_eager_steps():
+    """Stage 3: every layer's parameters gathered in forward order, then again in
+    reverse with the owned part of each layer's gradient reduced into the fp16
+    shard, then Adam into the rank's own fp16 parameter shard (which the next
+    step's gathers read), captured once and replayed."""
+    psi, nd, rank, seed, replays = 600_011, 4, 1, 47, 3
+    layers = [(0, 90_001), (90_001, 150_000), (240_001, 120_007), (360_008, 240_003)]
+    geom = Z.shard_geometry(psi, nd, rank)
+    lo, n = geom.offset, geom.len
+    s_all = -(-psi // nd)
+    rows = {}
+    for off, ln in layers:
+        a, b = Z.bucket_intersect(geom, off, ln)
+        if a < b:
+            rows[off] = (a, b - a, rows_device(seed, nd, a, b - a, wl.Dist(1e-3)))
+
+    def state():
+        shards = torch.empty((nd, s_all), dtype=torch.int16, device="cuda")
+        shards.copy_(torch.from_numpy(
+            np.random.default_rng(seed).integers(0, 0x3C00, size=(nd, s_all), dtype=np.int16)))
+        return {"shards": shards,
+                "master": state_device(seed, lo, n, wl.Dist(0.02), gen.KIND_MASTER),
+                "m": state_device(seed, lo, n, wl.Dist(1e-4), gen.KIND_M),
+                "v": state_device(seed, lo, n, wl.Dist(1e-6, True), gen.KIND_V),
+                "grad": torch.zeros(n, dtype=torch.int16, device="cuda"),
+                "layer": torch.zeros(max(ln for _, ln in layers), dtype=torch.int16,
+                                     device="cuda")}
+
+    def step(st, stream=None):
+        for off, ln in layers:                                   # forward
+            Z.gather_params(psi, nd, off, ln, st["shards"], st["layer"][:ln], stream=stream)
+        for off, ln in reversed(layers):                         # backward
+            Z.gather_params(psi, nd, off, ln, st["shards"], st["layer"][:ln], stream=stream)
+            if off in rows:
+                a, k, r = rows[off]
+                Z.reduce_shard(geom, a, k, r, None, st["grad"], stream=stream)
+        Z.adam_step_shard(geom, st["master"], st["m"], st["v"], st["grad"],
+                          st["shards"][rank, :n], lo, 1e-4, 0.9, 0.999, 1e-8, 1, stream=stream)
+
+    eager, graphed = state(), state()
+    warm = state()
+    step(warm)
+    torch.cuda.synchronize()
+    del warm
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(graphed, stream=side)
+    torch.cuda.synchronize()
+    for r in range(replays):
+        step(eager)
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in ("master", "m", "v"):
+            assert_bits(f32(graphed[key]), f32(eager[key]), f"replay {r} {key}")
+        for key in ("grad", "shards", "layer"):
+            assert_bits(u16(graphed[key]), u16(eager[key]), f"replay {r} {key}")
