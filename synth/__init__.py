@@ -2,5 +2,7 @@
 
 ``synth.gen`` (NumPy) and ``synth.device`` (HIP, via ctypes) implement one
 counter-based generator; ``synth.workloads`` holds the workload sizes and
-bucket schedules.  Nothing here computes any part of the ZeRO method.
+bucket schedules; ``synth.probe`` streams plain reads, writes and copies whose
+rates the bench reports as the box's practical HBM ceilings.  Nothing here
+computes any part of the ZeRO method.
 """
