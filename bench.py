@@ -580,7 +580,8 @@ def _oracle_time(w, inputs):
 def cpu_baseline(w, geom, chunk, target_s):
     """The oracle on the host, single-threaded, over consecutive chunks of the shard
     until about target_s seconds of oracle work (inputs are generated first, in a
-    worker pool, and are not timed)."""
+    worker pool, and are not timed).  Worker pools start fresh interpreters
+    ("spawn"): a forked child would inherit this process's GPU state."""
     import multiprocessing as mp
     first = _oracle_inputs((w, geom.offset, min(chunk, geom.len)))
     t_red, t_adam = _oracle_time(w, first)
@@ -591,7 +592,7 @@ def cpu_baseline(w, geom, chunk, target_s):
     if more > 0:
         jobs = [(w, geom.offset + n_done + i * chunk, chunk) for i in range(more)]
         workers = max(1, min(16, len(os.sched_getaffinity(0)) - 1, more))
-        with mp.get_context("fork").Pool(workers) as pool:
+        with mp.get_context("spawn").Pool(workers) as pool:
             inputs = pool.map(_oracle_inputs, jobs)
         for inp in inputs:
             a, b = _oracle_time(w, inp)
@@ -623,7 +624,7 @@ def cpu_baseline_all_cores(w, geom, chunk, chunks_per_worker=2):
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     n_chunks = min(workers * chunks_per_worker, -(-geom.len // chunk))
     jobs = [(w, geom.offset + i * chunk, min(chunk, geom.len - i * chunk)) for i in range(n_chunks)]
-    with mp.get_context("fork").Pool(workers) as pool:
+    with mp.get_context("spawn").Pool(workers) as pool:
         res = pool.map(_oracle_chunk_timed, jobs, chunksize=1)
     busy = {}
     for pid, _, t in res:
