@@ -126,7 +126,9 @@ int zero_shard_geometry(uint64_t psi, uint32_t nd, uint32_t rank, zero_geom_t *o
 
 /*
  * Flat range [*lo, *hi) of bucket [bucket_offset, bucket_offset + bucket_len)
- * that the rank owns; *lo == *hi when they do not meet.  Errors: ZERO_E_INVAL
+ * that the rank owns; *lo == *hi when they do not meet (card "ZeRO-2", the
+ * bucket diagram and "Gradient lifecycle": of each bucket reduce-scattered in
+ * backward, a rank keeps the part that falls in its own partition).  Errors: ZERO_E_INVAL
  * (null pointer, geometry that zero_shard_geometry would not return),
  * ZERO_E_RANGE (bucket beyond psi).
  */
@@ -205,7 +207,10 @@ typedef struct zero_shard {
 } zero_shard_t;
 
 /*
- * Per-step fp32 scalars of the Adam step, derived in fp64 and rounded once:
+ * Per-step fp32 scalars of the Adam step (Kingma & Ba, Algorithm 1: the
+ * bias corrections 1 - beta1^t and 1 - beta2^t of step t; the guide, "Como
+ * funciona", names mixed-precision Adam as the optimizer), derived in fp64 and
+ * rounded once:
  *   out[0] = b1 = RN32(beta1)          out[1] = b2 = RN32(beta2)
  *   out[2] = c1 = RN32(1 - beta1)      out[3] = c2 = RN32(1 - beta2)
  *   out[4] = e  = RN32(eps)
