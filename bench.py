@@ -213,15 +213,29 @@ def main():
 
     t_counter = [0]
 
+    def runs_of(ops):
+        """Consecutive launches of one kernel kind: [(kind, launches), ...]."""
+        runs = []
+        for kind, _, _ in ops:
+            if runs and runs[-1][0] == kind:
+                runs[-1][1] += 1
+            else:
+                runs.append([kind, 1])
+        return runs
+
     def step(events=None):
+        """One step; with events, one is recorded before each run of launches of
+        one kind and one after the step's last launch."""
         t_counter[0] += 1
         ops = launches(t_counter[0])
-        for i, (_, _, fn) in enumerate(ops):
-            if events is not None:
-                events[i][0].record(stream)
+        prev, r = None, 0
+        for kind, _, fn in ops:
+            if events is not None and kind != prev:
+                events[r].record(stream)
+                r, prev = r + 1, kind
             fn()
-            if events is not None:
-                events[i][1].record(stream)
+        if events is not None:
+            events[r].record(stream)
         return ops
 
     def ev():
@@ -230,45 +244,36 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # The timed steps hold nothing but the path's own launches: one event before
-    # and one after them.
-    start, end = ev(), ev()
+    # The timed steps: besides the path's own launches the stream holds only the
+    # events at the boundaries of each run of one kernel kind (3 per step for
+    # stage 2), so the per-kernel figures come from the timed region itself.
+    runs = runs_of(launches(1))
+    per_step = [[ev() for _ in range(len(runs) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(stream)
     ops = None
-    for _ in range(args.steps):
-        ops = step()
-    end.record(stream)
+    for k in range(args.steps):
+        ops = step(per_step[k])
     enqueued = time.perf_counter() - wall0         # host time to issue the timed steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
+    total_ms = per_step[0][0].elapsed_time(per_step[-1][-1])
     ms_step = total_ms / args.steps
-    # The per-kernel breakdown: as many steps again, each launch between two events.
-    per_step = [[(ev(), ev()) for _ in range(len(ops))] for _ in range(args.steps)]
-    start_i, end_i = ev(), ev()
-    torch.cuda.synchronize()
-    start_i.record(stream)
-    for k in range(args.steps):
-        step(per_step[k])
-    end_i.record(stream)
-    torch.cuda.synchronize()
-    instrumented_ms_step = start_i.elapsed_time(end_i) / args.steps
 
-    # ---- per-kernel figures from the per-launch events ------------------------------------
+    # ---- per-kernel figures from the run events ----------------------------------------
     names = {"reduce": "reduce_kernel", "adam": "adam_vec_kernel", "gather": "copy_kernel"}
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
     kernels = {}
-    for kind in dict.fromkeys(k for k, _, _ in ops):
-        idx = [i for i, (k, _, _) in enumerate(ops) if k == kind]
-        bytes_step = sum(ops[i][1] for i in idx)
-        per = [sum(per_step[s][i][0].elapsed_time(per_step[s][i][1]) for i in idx)
+    for kind in dict.fromkeys(k for k, _ in runs):
+        rs = [r for r, (k, _) in enumerate(runs) if k == kind]
+        n_launch = sum(runs[r][1] for r in rs)
+        bytes_step = sum(b for k, b, _ in ops if k == kind)
+        per = [sum(per_step[s][r].elapsed_time(per_step[s][r + 1]) for r in rs)
                for s in range(args.steps)]
         avg_step = sum(per) / args.steps
         kernels[kind] = {
-            "kernel": names[kind], "launches_per_step": len(idx),
-            "avg_ms_per_launch": avg_step / len(idx), "avg_ms_per_step": avg_step,
+            "kernel": names[kind], "launches_per_step": n_launch,
+            "avg_ms_per_launch": avg_step / n_launch, "avg_ms_per_step": avg_step,
             "min_ms_per_step": min(per), "median_ms_per_step": float(np.median(per)),
             "bytes_per_step": bytes_step,
             "bytes_per_element": bytes_step / S,
@@ -315,7 +320,6 @@ def main():
         "ms_per_step": ms_step,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
-        "instrumented_ms_per_step": instrumented_ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "hbm_gbs": gbs(step_bytes, ms_step),
