@@ -200,3 +200,104 @@ def _state_probe(w, lo, n):
         sdev.fill_state(t, w.seed, kind, lo, d.sigma, d.absolute)
         out.append(t)
     return out
+
+
+def test_fullsize_zero3_7p5b_rank0():
+    """Stage 3 at 7.5B / Nd = 64, rank 0, one step as the bench runs it: every layer
+    gathered in forward order, then again in reverse with the owned layer's
+    gradient reduced into the fp16 shard, then Adam into the rank's own fp16
+    parameter shard.  Sampled against the oracle: a gathered layer crossing two
+    other ranks' shards (their generated fp16 parameters), the fp16 gradient
+    shard, the state after the step, and a gather after the step that must return
+    the updated own shard where the layer crosses it."""
+    w = wl.zero3_7p5b(0)
+    psi, nd, rank = w.psi, w.nd, w.rank
+    geom = Z.shard_geometry(psi, nd, rank)
+    lo, S = geom.offset, geom.len
+    print(f"{w.name}: shard [{lo}, +{S})", flush=True)
+    s_all = -(-psi // nd)
+    sigma_p = w.extra["param_sigma"]
+    shards = torch.empty((nd, s_all), dtype=torch.int16, device="cuda")
+    for k in range(nd):
+        k_lo = min(k * s_all, psi)
+        k_n = min((k + 1) * s_all, psi) - k_lo
+        if k_n:
+            sdev.fill_grad_rows(shards[k:k + 1, :k_n], w.seed, k_lo, sigma_p, rank0=k,
+                                kind=gen.KIND_PARAM16)
+    state = _state(w, geom)
+    grad16 = torch.zeros(S, dtype=torch.int16, device="cuda")
+    layers = list(reversed(w.buckets))                          # forward order
+    layer_buf = torch.empty(max(n for _, n in layers), dtype=torch.int16, device="cuda")
+    rng = np.random.default_rng(9)
+
+    def owner_values(flat):
+        k = (flat // np.uint64(s_all)).astype(np.int64)
+        out = np.empty(flat.size, np.uint16)
+        for kk in np.unique(k):
+            sel = k == kk
+            out[sel] = gen.grad_f16(w.seed, int(kk), flat[sel], sigma_p, kind=gen.KIND_PARAM16)
+        return out, k
+
+    # forward: check the layers that cross two shards, neither of them this rank's
+    crossing_checked = 0
+    for off, n in layers:
+        Z.gather_params(psi, nd, off, n, shards, layer_buf[:n])
+        if off // s_all >= 2 and (off + n - 1) // s_all == off // s_all + 1:
+            torch.cuda.synchronize()
+            rel = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                            rng.integers(0, n, 4096)])).astype(np.int64)
+            want, _ = owner_values(rel.astype(np.uint64) + np.uint64(off))
+            got = layer_buf.index_select(0, torch.from_numpy(rel).cuda()).cpu().numpy()
+            assert_bits(got.view(np.uint16), want, f"forward gather of layer at {off}")
+            crossing_checked += 1
+    assert crossing_checked > 0
+    # backward: gather, then reduce the owned part of the layer's gradient
+    edges = []
+    for off, n in w.buckets:
+        Z.gather_params(psi, nd, off, n, shards, layer_buf[:n])
+        a, b = Z.bucket_intersect(geom, off, n)
+        if a < b:
+            edges += [a - lo, b - lo]
+            st = Z.row_stride(b - a)
+            buf = torch.empty(nd * st, dtype=torch.int16, device="cuda")
+            rows = buf.as_strided((nd, b - a), (st, 1))
+            sdev.fill_grad_rows(rows, w.seed, a, w.grad.sigma, w.grad.heavy_tail)
+            Z.reduce_shard(geom, a, b - a, rows, None, grad16)
+            del rows, buf
+    torch.cuda.synchronize()
+    idx = sample_indices(S, edges, N_RANDOM, seed=21)
+    flat = idx.astype(np.uint64) + np.uint64(lo)
+    g32 = _oracle_grad(w, flat)
+    g16_ref = g32.astype(np.float16).view(np.uint16)
+    assert_bits(gather(grad16, idx).cpu().numpy().view(np.uint16), g16_ref, "fp16 gradient shard")
+    # Adam into the own shard (row `rank` of the shard buffer, origin = shard offset)
+    it = torch.from_numpy(idx).cuda()
+    before = [x.index_select(0, it).cpu().numpy() for x in state]
+    Z.adam_step_shard(geom, *state, grad16, shards[rank, :S], lo, w.lr, w.beta1, w.beta2,
+                      w.eps, 1)
+    torch.cuda.synchronize()
+    after = [x.index_select(0, it).cpu().numpy() for x in state]
+    sc = oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, 1)
+    want = oadam.step_values(*before, g16_ref, sc)
+    for got, exp, name in zip(after, want[:3], ("master", "m", "v")):
+        assert_bits(got, exp, f"{name} after the step")
+    p16 = shards[rank, :S].index_select(0, it).cpu().numpy().view(np.uint16)
+    assert_bits(p16, want[3], "own fp16 shard after the step")
+    # the next gather of the layer that holds the shard's end sees the update
+    last = lo + S - 1
+    off, n = next((o, k) for o, k in layers if o <= last < o + k)
+    Z.gather_params(psi, nd, off, n, shards, layer_buf[:n])
+    torch.cuda.synchronize()
+    rel = np.unique(np.concatenate([np.clip(np.arange(last - off - 63, last - off + 65), 0, n - 1),
+                                    rng.integers(0, n, 4096)])).astype(np.int64)
+    fl = rel.astype(np.uint64) + np.uint64(off)
+    want_g, owner = owner_values(fl)
+    mine = owner == rank
+    pos = np.searchsorted(flat, fl[mine])
+    known = (pos < flat.size) & (flat[np.minimum(pos, flat.size - 1)] == fl[mine])
+    got = layer_buf.index_select(0, torch.from_numpy(rel).cuda()).cpu().numpy().view(np.uint16)
+    others = ~mine
+    assert_bits(got[others], want_g[others], "gathered elements of other ranks")
+    mine_idx = np.flatnonzero(mine)[known]
+    assert mine_idx.size > 0
+    assert_bits(got[mine_idx], want[3][pos[known]], "gathered elements of the own shard")
