@@ -19,7 +19,7 @@ import torch
 
 import zero_sharded_mixed_bucketed_amd as Z
 from gpu_util import assert_bits, f32, need_gpu, u16
-from synth import gen, workloads as wl
+from synth import gen
 
 pytestmark = pytest.mark.gpu
 

@@ -13,7 +13,6 @@ from gpu_util import (assert_adam_step, assert_bits, f32, need_gpu, rows_device,
 from oracle import adam as oadam
 from oracle import geometry as ogeo
 from oracle import reduce as ored
-from synth import device as sdev
 from synth import gen, workloads as wl
 
 pytestmark = pytest.mark.gpu

@@ -3,7 +3,6 @@
 library sources, with the sanitizers on the host side of the compilation only,
 and must run clean."""
 import os
-import shutil
 import subprocess
 
 import pytest
