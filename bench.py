@@ -20,7 +20,8 @@ from HIP events on the launch stream, the roofline of the dominant kernel, a
 sampled self-check against the CPU oracle, and the oracle's own throughput on
 the host as a baseline.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
+                    [--seed S] [--no-cpu-baseline] [--no-ceilings]
 """
 from __future__ import annotations
 
@@ -76,8 +77,10 @@ def workload(name, rank):
     if name == "zero2-100B-nd400":
         return wl.zero2_100b(137 if rank is None else rank)
     if name == "plain-dp-1.4B":
+        if rank not in (None, 0):
+            raise SystemExit("plain data parallelism has one rank (Nd = 1): --rank 0")
         return wl.plain_dp_1p4b()
-    return wl.tiny()
+    return wl.tiny(rank=0 if rank is None else rank)
 
 
 def main():

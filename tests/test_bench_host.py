@@ -40,6 +40,9 @@ def test_every_workload_choice_maps_to_a_workload():
         assert b.workload(arg, None).name == name
     assert b.workload("zero2-7.5B-nd64", 3).rank == 3
     assert b.workload("tiny-zero2", None).psi == 1 << 20
+    assert b.workload("tiny-zero2", 3).rank == 3
+    with pytest.raises(SystemExit):
+        b.workload("plain-dp-1.4B", 1)
 
 
 def _summary(dirpath, kernel, workload, sha, nbytes):
