@@ -77,9 +77,13 @@ def test_committed_summaries_are_well_formed():
         tracked = set(r.stdout.split())
     else:                                  # a copy of the tree without its history
         tracked = {p for p in ("bench.py",) if os.path.exists(os.path.join(ROOT, p))}
+    choices = ("zero2-7.5B-nd64", "zero2-7.5B-nd64-g16", "zero3-7.5B-nd64", "zero2-13B-nd32",
+               "zero2-100B-nd400", "plain-dp-1.4B", "tiny-zero2")
+    names = {b.workload(c, None).name for c in choices}
     for f in files:
         kernel, workload = f[:-3].split("__")
         assert kernel in b.KERNEL_SOURCES, f
+        assert workload in names, (f, "no bench workload has this name")
         text = open(os.path.join(pdir, f)).read()
         assert re.search(r"^- measured HBM bytes per launch: \d+$", text, re.M), f
         assert re.search(r"^- kernel source sha256: `[0-9a-f]{64}`$", text, re.M), f
