@@ -119,7 +119,8 @@ def test_reduce_unaligned(stride_pad, out_shift):
 @pytest.mark.parametrize("nd", [2, 15, 31, 33, 48, 63, 65, 97])
 def test_reduce_row_batches(nd):
     """Nd values whose rows split into every mix of the kernel's load batches
-    (32, then 16, 8, 4, 2, 1): the additions must stay in ascending rank order."""
+    (full batches of 16, then 8, 4, 2 and 1): the additions must stay in ascending
+    rank order."""
     print(f"reduce nd={nd}", flush=True)
     psi = 40_009 * nd
     _reduce_case(psi, nd, nd // 2, wl.uniform_buckets(psi, 17_001), wl.Dist(0.05), 2000 + nd)
