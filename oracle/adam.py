@@ -41,6 +41,10 @@ the closed form with m = v = 0 and a constant gradient (th_t = th_0 -
 t*lr*g/(|g| + eps) in real arithmetic); special cases (zero gradient from zero
 moments leaves th unchanged); and the sharded-equals-unsharded invariant over
 all ranks of a tiny model, including the rebuilt fp16 vector.
+
+Parity unpinned: the exact last bits of the step.  Where Algorithm 1 leaves the
+fp32 operation order open they follow the fixed order above; the pins hold them
+to within a few ulps of the term scale, not bit for bit.
 """
 from __future__ import annotations
 
