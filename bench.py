@@ -414,7 +414,20 @@ def environment(torch, dev):
             "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
             "hip": torch.version.hip, "torch": torch.__version__,
             "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0)),
+            "host_cpu_model": host_cpu_model(),
             "library_sources_sha256": library_sources_sha256()}
+
+
+def host_cpu_model():
+    """The host CPU's model name (the oracle baseline runs on it), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def library_sources_sha256():

@@ -103,3 +103,12 @@ def test_library_sources_digest_tracks_the_sources(tmp_path):
                 h.update(f.encode())
                 h.update(open(os.path.join(d, f), "rb").read())
     assert d1 == h.hexdigest()
+
+
+def test_host_cpu_model_is_named():
+    """The CPU baseline's host is named in the JSON's env: the first 'model name' of
+    /proc/cpuinfo, or None where the file has none."""
+    model = _bench().host_cpu_model()
+    with open("/proc/cpuinfo") as f:
+        names = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
+    assert model == (names[0] if names else None)
