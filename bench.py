@@ -109,7 +109,14 @@ def main():
           f"+{S})", file=sys.stderr, flush=True)
 
     # ---- inputs resident in HBM (untimed) ----------------------------------------------
+    # Generating them is not part of the metric; its time is reported on its own
+    # (wall time with the allocations, and the device time of the generator
+    # kernels on the stream between two events).
     shards = layer_buf = None
+    torch.cuda.synchronize()
+    setup_wall0 = time.perf_counter()
+    setup_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    setup_ev[0].record(stream)
     with torch.cuda.stream(stream):
         master = torch.empty(S, dtype=torch.float32, device=dev)
         m = torch.empty_like(master)
@@ -159,7 +166,13 @@ def main():
                     rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
                     sdev.fill_grad_rows(rows, w.seed, c0, w.grad.sigma, w.grad.heavy_tail)
                     buckets.append((c0, c1 - c0, rows))
+    setup_ev[1].record(stream)
     torch.cuda.synchronize()
+    input_setup = {"wall_s": time.perf_counter() - setup_wall0,
+                   "device_ms": setup_ev[0].elapsed_time(setup_ev[1]),
+                   "bytes_resident": torch.cuda.memory_allocated(),
+                   "what": "seeded synthetic inputs generated on the device (untimed, not in "
+                           "value)"}
     init_idx = None
     if args.check_samples:
         rng = np.random.default_rng(1)
@@ -347,6 +360,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "ceilings": ceilings,
+        "input_setup": input_setup,
         "env": environment(torch, dev),
     }
     print(json.dumps(out), flush=True)
