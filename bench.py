@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import gc
 import json
 import os
 import sys
@@ -257,6 +258,12 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # Python's cyclic garbage collector stays off from the warm-up to the end of
+    # the timed steps: a full collection takes tens of milliseconds on the host,
+    # and one falling between two timed steps left the GPU idle for as long once
+    # the launches already queued had drained.
+    gc.collect()
+    gc.disable()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -273,6 +280,7 @@ def main():
     enqueued = time.perf_counter() - wall0         # host time to issue the timed steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = per_step[0][0].elapsed_time(per_step[-1][-1])
     ms_step = total_ms / args.steps
 
@@ -315,9 +323,8 @@ def main():
 
     ceilings = None
     if not args.no_ceilings:
-        widest = max((n for _, n, _ in buckets), default=None)
-        ceilings = stream_ceilings(torch, dev, stream,
-                                   (w.nd, widest) if widest else None)
+        widest = max(buckets, key=lambda b: b[1], default=None)
+        ceilings = stream_ceilings(torch, dev, stream, widest[2] if widest else None)
         if "reduce" in kernels and "read_rows_gbs" in ceilings:
             ceilings["reduce_of_read_rows"] = kernels["reduce"]["gbs"] / ceilings["read_rows_gbs"]
 
@@ -366,18 +373,19 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def stream_ceilings(torch, dev, stream, rows_shape=None, nbytes=4 << 30, reps=10):
+def stream_ceilings(torch, dev, stream, rows=None, nbytes=4 << 30, reps=10):
     """Practical HBM rates on the same box, timed with HIP events on the launch
     stream after the measurement; context for the kernels' rates.
 
-    - read_rows: the reduce's access pattern over Nd rows of the workload's widest
-      launch (at most nbytes of rows), without its arithmetic and stores, at the
-      reduce's occupancy cap;
+    - read_rows: the reduce's access pattern, without its arithmetic and stores,
+      at the reduce's occupancy cap, over the very rows of the workload's widest
+      reduce launch (their first columns, a multiple of 8, at most nbytes): the
+      read rate of one allocation moves by several per cent with where it lands,
+      so the reduce is compared with a read of the same memory;
     - write, copy: 16-byte stores / non-temporal loads and stores over nbytes,
       no occupancy cap;
     - runtime_copy, runtime_fill: torch's own device copy_ and fill_ over nbytes.
     """
-    import zero_sharded_mixed_bucketed_amd as Z
     from synth import probe
 
     def timed(fn):
@@ -393,18 +401,17 @@ def stream_ceilings(torch, dev, stream, rows_shape=None, nbytes=4 << 30, reps=10
 
     gbs = lambda moved, ms: moved / (ms * 1e-3) / 1e9
     out = {}
-    if rows_shape is not None:
-        nd, cols = rows_shape
+    if rows is not None:
+        nd, cols = rows.shape
         cols = min(cols, nbytes // (2 * nd)) // 8 * 8
-        stride = Z.row_stride(cols)
+        view = rows[:, :cols]
         with torch.cuda.stream(stream):
-            buf = torch.ones(nd * stride, dtype=torch.int16, device=dev)
             sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        rows = buf.as_strided((nd, cols), (stride, 1))
-        ms = timed(lambda: probe.read_rows(rows, sink, 8, stream=stream))
+        ms = timed(lambda: probe.read_rows(view, sink, 8, stream=stream))
         out["read_rows_gbs"] = gbs(2 * nd * cols, ms)
-        out["read_rows_shape"] = [nd, cols, stride]
-        del rows, buf, sink
+        out["read_rows_shape"] = [nd, cols, rows.stride(0)]
+        out["read_rows_source"] = "the rows of the widest reduce launch"
+        del view, sink
     n = nbytes // 4
     with torch.cuda.stream(stream):
         src = torch.ones(n, dtype=torch.float32, device=dev)
