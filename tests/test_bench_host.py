@@ -112,3 +112,14 @@ def test_host_cpu_model_is_named():
     with open("/proc/cpuinfo") as f:
         names = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
     assert model == (names[0] if names else None)
+
+
+def test_timed_steps_run_with_the_garbage_collector_off():
+    """A full collection of Python's cyclic garbage collector (tens of ms on the host)
+    between two timed steps leaves the GPU idle once the queued launches drain, so
+    the collector is disabled from the warm-up to the end of the timed steps."""
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    main = src[src.index("def main():"):src.index("\ndef ", src.index("def main():") + 1)]
+    off, warm = main.index("gc.disable()"), main.index("for _ in range(args.warmup):")
+    timed, on = main.index("for k in range(args.steps):"), main.index("gc.enable()")
+    assert off < warm < timed < on
