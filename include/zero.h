@@ -36,8 +36,9 @@
  *    zero_last_error() returns a message for the calling thread's last error.
  *    Non-finite values in the data are not errors; they propagate per IEEE.
  *  - Several threads may call at once.  The only process-wide state is a cache
- *    of each device's compute-unit count and LDS size, filled atomically on
- *    first use; the error message is per thread.
+ *    of each device's compute-unit count and the dynamic LDS sizes that cap
+ *    the streaming kernels' residency (zero_launch_occupancy), resolved under a
+ *    lock on first use; the error message is per thread.
  */
 #ifndef ZERO_H_
 #define ZERO_H_
@@ -268,6 +269,30 @@ int zero_adam_step_shard(const zero_geom_t *g, const zero_shard_t *s, double lr,
 int zero_gather_params(uint64_t psi, uint32_t nd, uint64_t lo, uint64_t len,
                        const uint16_t *shards, uint64_t shard_stride, uint16_t *out,
                        void *hip_stream);
+
+/* The streaming kernels whose residency the library caps (zero_launch_occupancy). */
+#define ZERO_KERNEL_REDUCE_W16 0 /* the reduce with 16-byte row loads (aligned rows) */
+#define ZERO_KERNEL_REDUCE_W8 1  /* ... 8-byte row loads */
+#define ZERO_KERNEL_REDUCE_W4 2  /* ... 4-byte row loads */
+#define ZERO_KERNEL_REDUCE_W2 3  /* ... 2-byte row loads */
+#define ZERO_KERNEL_ADAM_G32 4   /* the fused Adam step, fp32 gradient */
+#define ZERO_KERNEL_ADAM_G16 5   /* the fused Adam step, fp16 gradient */
+
+/*
+ * Launch residency of one capped kernel on the calling thread's current device.
+ * No passage defines it: it is a measured property of MI355X.  The reduce and
+ * the Adam step stream HBM faster when fewer workgroups share a compute unit
+ * (at most 8 for the reduce, 10 for Adam), so every launch asks for dynamic
+ * LDS that the kernels never touch.  On the first call that launches on a
+ * device, the library resolves, per kernel, the LDS size at which the
+ * runtime's occupancy calculator allows exactly that many workgroups per CU,
+ * and it refuses to launch (ZERO_E_DEVICE) when no size does.
+ * Fills *wgs_per_cu with the workgroups per CU the calculator allows at the
+ * resolved size, and *lds_bytes (nullable) with that size.
+ * Errors: ZERO_E_INVAL (unknown kernel, wgs_per_cu NULL), ZERO_E_DEVICE (no
+ * device, or the cap cannot be reached on it).
+ */
+int zero_launch_occupancy(int kernel, int *wgs_per_cu, uint32_t *lds_bytes);
 
 /* Message of the calling thread's last error ("" if none).  Valid until the
  * thread's next call into the library. */

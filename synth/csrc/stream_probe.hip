@@ -16,6 +16,12 @@
 // workgroups are dispatched, and non-temporal stores write no faster here.
 // Each launch can cap the workgroups per compute unit with dynamic LDS that the
 // kernel never touches (the device the path's kernels use).
+//
+//  - residency: each one-wavefront workgroup sleeps for a fixed time and its
+//    first lane records the compute unit it ran on and the wall-clock interval
+//    it spanned; the most intervals that overlap on one compute unit is the
+//    number of workgroups resident there at once, under a given dynamic LDS
+//    size.  It checks that an LDS size really caps residency on the hardware.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,8 +79,34 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const u32x4* src, u32x4*
   if (gi < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + gi), dst + gi);
 }
 
+// A compute unit's identity: XCC (hardware register XCC_ID, bits 3:0) above
+// bits 8..14 of HW_ID (CU_ID 11:8, SH_ID 12, SE_ID 14:13 on gfx950).
+__device__ __forceinline__ uint32_t cu_key() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID, 32 bits
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);   // XCC_ID, 4 bits
+  return ((xcc & 0xFu) << 8) | ((hw >> 8) & 0x7Fu);
+}
+
+// rec[3 b .. 3 b + 2] = {start, end, cu_key} of workgroup b; `sleeps` rounds of
+// s_sleep (a bounded loop: every wave exits).
+__global__ void __launch_bounds__(kThreads) residency_kernel(unsigned long long* rec,
+                                                            uint32_t sleeps) {
+  const unsigned long long t0 = static_cast<unsigned long long>(wall_clock64());
+  for (uint32_t i = 0; i < sleeps; ++i) __builtin_amdgcn_s_sleep(8);
+  const unsigned long long t1 = static_cast<unsigned long long>(wall_clock64());
+  if (threadIdx.x == 0) {
+    unsigned long long* r = rec + 3ull * blockIdx.x;
+    r[0] = t0;
+    r[1] = t1;
+    r[2] = cu_key();
+  }
+}
+
 // Dynamic LDS per workgroup that limits a compute unit to `wgs` workgroups (0:
-// no cap), or -1 if the device cannot be queried.
+// no cap), or -1 if the device cannot be queried: the CU's LDS over `wgs`,
+// rounded down to the 1,280-byte granule in which gfx950 allocates LDS (a size
+// between granules is rounded up by the hardware and can hold one workgroup
+// fewer).
 long cap_bytes(int wgs) {
   if (wgs <= 0) return 0;
   int dev = 0, lds = 0;
@@ -82,7 +114,7 @@ long cap_bytes(int wgs) {
   if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
       hipSuccess)
     return -1;
-  return static_cast<long>(lds / wgs) / 512 * 512;
+  return static_cast<long>(lds / wgs) / 1280 * 1280;
 }
 
 bool grid_of(uint64_t items, unsigned* blocks, uint64_t threads = kThreads) {
@@ -141,6 +173,18 @@ int zprobe_copy(const void* src, void* dst, uint64_t bytes, int wgs_per_cu, void
   hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(kThreads), static_cast<unsigned>(cap),
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Runs `blocks` residency workgroups with `lds_bytes` of dynamic LDS each; rec
+// (device, 8-byte aligned) receives 3 * blocks values.  sleeps <= 100000.
+int zprobe_residency(unsigned long long* rec, uint32_t blocks, uint32_t lds_bytes, uint32_t sleeps,
+                     void* stream) {
+  if (!rec || blocks == 0 || blocks > 0x7FFFFFFFu || sleeps > 100000 ||
+      reinterpret_cast<uintptr_t>(rec) % 8)
+    return -1;
+  hipLaunchKernelGGL(residency_kernel, dim3(blocks), dim3(kThreads), lds_bytes,
+                     static_cast<hipStream_t>(stream), rec, sleeps);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -27,6 +27,8 @@ def _load():
         lib.zprobe_write.restype = ci
         lib.zprobe_copy.argtypes = [vp, vp, u64, ci, vp]
         lib.zprobe_copy.restype = ci
+        lib.zprobe_residency.argtypes = [vp, u32, u32, u32, vp]
+        lib.zprobe_residency.restype = ci
         _lib = lib
     return _lib
 
@@ -76,3 +78,31 @@ def copy(src: torch.Tensor, dst: torch.Tensor, wgs_per_cu: int = 10, stream=None
         raise ValueError("src and dst must be contiguous device tensors of the same size")
     _check(_load().zprobe_copy(src.data_ptr(), dst.data_ptr(), nbytes, wgs_per_cu,
                                _stream(stream)), "zprobe_copy")
+
+
+def residency(rec: torch.Tensor, blocks: int, lds_bytes: int, sleeps: int = 100,
+              stream=None) -> None:
+    """Launch `blocks` one-wavefront workgroups with `lds_bytes` of dynamic LDS;
+    rec (int64 device tensor of >= 3 * blocks elements) receives per workgroup
+    its start and end wall-clock ticks and its compute unit's key."""
+    if rec.dtype != torch.int64 or not rec.is_cuda or not rec.is_contiguous() \
+            or rec.numel() < 3 * blocks:
+        raise ValueError("rec must be a contiguous int64 device tensor of >= 3 * blocks")
+    _check(_load().zprobe_residency(rec.data_ptr(), blocks, lds_bytes, sleeps, _stream(stream)),
+           "zprobe_residency")
+
+
+def max_resident(rec) -> dict:
+    """From residency()'s records (host int64 [blocks, 3]): the most workgroups
+    whose intervals overlap on each compute unit."""
+    import numpy as np
+    rec = np.asarray(rec).reshape(-1, 3)
+    out = {}
+    for key in np.unique(rec[:, 2]):
+        r = rec[rec[:, 2] == key]
+        # ends sort before starts at equal ticks: touching intervals do not overlap
+        ev = np.concatenate([np.stack([r[:, 0], np.ones(len(r), np.int64)], 1),
+                             np.stack([r[:, 1], -np.ones(len(r), np.int64)], 1)])
+        ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]
+        out[int(key)] = int(np.max(np.cumsum(ev[:, 1])))
+    return out

@@ -118,6 +118,12 @@ int main() {
   EXPECT(zero_gather_params(100, 4, 10, 10, fake16, 1ull << 62, fake16, NULL) == ZERO_E_RANGE);
   EXPECT(zero_gather_params(100, 4, 10, 0, NULL, 0, NULL, NULL) == ZERO_OK);
 
+  int wgs = 0;
+  uint32_t lds = 0;
+  EXPECT(zero_launch_occupancy(6, &wgs, &lds) == ZERO_E_INVAL);
+  EXPECT(zero_launch_occupancy(-1, &wgs, NULL) == ZERO_E_INVAL);
+  EXPECT(zero_launch_occupancy(ZERO_KERNEL_ADAM_G32, NULL, &lds) == ZERO_E_INVAL);
+
   if (g_fail) return 1;
   printf("abi host check ok\n");
   return 0;

@@ -323,3 +323,16 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_launch_occupancy_rejects_before_any_device_call():
+    """An unknown kernel or a NULL output is refused before the library asks for
+    the device (no GPU here)."""
+    wgs, lds = ctypes.c_int(-7), ctypes.c_uint32(7)
+    for kernel in (-1, 6, 1000):
+        assert Z.lib.zero_launch_occupancy(kernel, ctypes.byref(wgs), ctypes.byref(lds)) \
+            == Z.ZERO_E_INVAL
+        assert "unknown kernel" in Z.last_error()
+    assert Z.lib.zero_launch_occupancy(Z.KERNEL_REDUCE_W16, None, ctypes.byref(lds)) \
+        == Z.ZERO_E_INVAL
+    assert (wgs.value, lds.value) == (-7, 7)

@@ -1,0 +1,79 @@
+"""The residency cap of the two streaming kernels is resolved on the device and
+holds on the hardware.
+
+The reduce runs at most 8 and the Adam step at most 10 workgroups per compute
+unit: on MI355X fewer concurrent access streams per CU move more bytes per
+second, so each launch asks for dynamic LDS that the kernel never touches.  The
+library resolves that LDS size per device with the runtime's occupancy
+calculator on the kernel itself (zero_launch_occupancy reports it).  These
+tests check the calculator's figure through the C ABI, and then that the same
+LDS size caps residency on the hardware: a probe kernel launched with it
+records, per workgroup, its compute unit and the wall-clock interval it spans,
+and the most intervals that overlap on one CU must equal the cap.  A runtime
+that mis-reports the LDS size of a CU would pass the first check and fail the
+second -- as it did before the library searched only multiples of 2,560
+bytes: gfx950 hands out LDS in 1,280-byte granules while the calculator rounds
+to 512, so at 16,384 bytes it reported 10 workgroups per CU where the hardware
+held 9.
+"""
+import numpy as np
+import pytest
+import torch
+
+import zero_sharded_mixed_bucketed_amd as Z
+from gpu_util import need_gpu
+from synth import probe
+
+pytestmark = pytest.mark.gpu
+
+CAPS = [(Z.KERNEL_REDUCE_W16, 8), (Z.KERNEL_REDUCE_W8, 8), (Z.KERNEL_REDUCE_W4, 8),
+        (Z.KERNEL_REDUCE_W2, 8), (Z.KERNEL_ADAM_G32, 10), (Z.KERNEL_ADAM_G16, 10)]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    print(flush=True)
+
+
+@pytest.mark.parametrize("kernel,want", CAPS)
+def test_launch_occupancy_is_the_cap(kernel, want):
+    wgs, lds = Z.launch_occupancy(kernel)
+    print(f"kernel {kernel}: {wgs} workgroups per CU at {lds} bytes of dynamic LDS", flush=True)
+    assert wgs == want
+    # a multiple of both the hardware's 1,280-byte LDS granule and the
+    # calculator's 512 bytes, so neither rounds it
+    assert 0 < lds <= 64 * 1024 and lds % 2560 == 0
+
+
+def test_launch_occupancy_rejects_unknown_kernel():
+    with pytest.raises(Z.ZeroError) as e:
+        Z.launch_occupancy(6)
+    assert e.value.code == Z.ZERO_E_INVAL
+
+
+def _resident(lds, blocks):
+    rec = torch.zeros(3 * blocks, dtype=torch.int64, device="cuda")
+    probe.residency(rec, blocks, lds, sleeps=100)
+    torch.cuda.synchronize()
+    return probe.max_resident(rec.cpu().numpy())
+
+
+@pytest.mark.parametrize("kernel,want", [(Z.KERNEL_REDUCE_W16, 8), (Z.KERNEL_ADAM_G32, 10),
+                                         (Z.KERNEL_ADAM_G16, 10)])
+def test_resolved_lds_caps_hardware_residency(kernel, want):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 64 * cus                   # twice what the widest residency holds at once
+    _, lds = Z.launch_occupancy(kernel)
+    per_cu = _resident(lds, blocks)
+    counts = np.array(list(per_cu.values()))
+    print(f"lds {lds}: {len(per_cu)} CUs, resident per CU min {counts.min()} "
+          f"median {np.median(counts)} max {counts.max()}", flush=True)
+    assert len(per_cu) == cus          # one key per compute unit: the decoding holds
+    assert counts.max() == want
+    assert np.median(counts) == want
+    # without the LDS request the same probe holds more workgroups per CU, so the
+    # probe itself does not cap residency at the figure above
+    free = np.array(list(_resident(0, blocks).values()))
+    print(f"no LDS: resident per CU median {np.median(free)} max {free.max()}", flush=True)
+    assert np.median(free) > want

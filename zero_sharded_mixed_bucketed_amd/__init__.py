@@ -15,6 +15,7 @@ names follow the C ABI in ``include/zero.h``:
     adam_step_shard(geom, master, m, v, grad, param16, param16_origin,
                     lr, beta1, beta2, eps, step)
     gather_params(psi, nd, lo, length, shards, out)
+    launch_occupancy(kernel)                    -> (workgroups per CU, dynamic LDS bytes)
 
 Importing this package fails if libzero.so has not been built: there is no
 fallback path.
@@ -40,7 +41,11 @@ STAGE_DP, STAGE_OS, STAGE_OS_G, STAGE_OS_G_P = 0, 1, 2, 3
 EXPORTS = ("zero_memory_model", "zero_memory_model_k", "zero_comm_volume",
            "zero_shard_geometry", "zero_bucket_intersect", "zero_row_stride",
            "zero_reduce_shard", "zero_adam_scalars", "zero_adam_step_shard",
-           "zero_gather_params", "zero_last_error")
+           "zero_gather_params", "zero_launch_occupancy", "zero_last_error")
+
+# Kernels of zero_launch_occupancy.
+KERNEL_REDUCE_W16, KERNEL_REDUCE_W8, KERNEL_REDUCE_W4, KERNEL_REDUCE_W2 = 0, 1, 2, 3
+KERNEL_ADAM_G32, KERNEL_ADAM_G16 = 4, 5
 
 
 class ZeroError(RuntimeError):
@@ -116,6 +121,8 @@ def _load() -> ctypes.CDLL:
     lib.zero_adam_step_shard.restype = ci
     lib.zero_gather_params.argtypes = [u64, u32, u64, u64, vp, u64, vp, vp]
     lib.zero_gather_params.restype = ci
+    lib.zero_launch_occupancy.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(u32)]
+    lib.zero_launch_occupancy.restype = ci
     lib.zero_last_error.argtypes = []
     lib.zero_last_error.restype = ctypes.c_char_p
     return lib
@@ -181,6 +188,17 @@ def adam_scalars(lr: float, beta1: float, beta2: float, eps: float, step: int):
     out = (ctypes.c_float * 7)()
     _check(lib.zero_adam_scalars(lr, beta1, beta2, eps, step, out))
     return tuple(out)
+
+
+def launch_occupancy(kernel: int, device=None) -> Tuple[int, int]:
+    """(workgroups per CU, dynamic LDS bytes) of a capped kernel's launches on
+    `device` (default: the current device)."""
+    import torch
+    wgs, lds = ctypes.c_int(), ctypes.c_uint32()
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    with torch.cuda.device(dev):
+        _check(lib.zero_launch_occupancy(kernel, ctypes.byref(wgs), ctypes.byref(lds)))
+    return wgs.value, lds.value
 
 
 def _one_device(tensors, stream):

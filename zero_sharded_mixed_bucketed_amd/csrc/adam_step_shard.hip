@@ -26,9 +26,8 @@
 namespace zero {
 namespace {
 
-constexpr int kThreads = 64;    // one wavefront per workgroup
-constexpr int kWgsPerCu = 10;   // occupancy cap of the vector kernel
-constexpr int kVec = 4;         // elements per thread (16-byte accesses of the fp32 arrays)
+constexpr int kThreads = kAdamThreads;  // one wavefront per workgroup
+constexpr int kVec = 4;                 // elements per thread (16-byte accesses of the fp32 arrays)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -154,7 +153,12 @@ __global__ void __launch_bounds__(kThreads) adam_scalar_kernel(Args a, uint64_t 
 
 }  // namespace
 
-hipError_t launch_adam(const AdamLaunch& L, const DeviceInfo& d, hipStream_t stream) {
+const void* adam_kernel_fn(int grad_is_fp16) {
+  return grad_is_fp16 ? reinterpret_cast<const void*>(&adam_vec_kernel<true>)
+                      : reinterpret_cast<const void*>(&adam_vec_kernel<false>);
+}
+
+hipError_t launch_adam(const AdamLaunch& L, const DeviceCaps& d, hipStream_t stream) {
   Args a;
   a.master = L.master;
   a.m = L.m;
@@ -175,11 +179,13 @@ hipError_t launch_adam(const AdamLaunch& L, const DeviceInfo& d, hipStream_t str
     const uint64_t want = (a.ngroups + kThreads - 1) / kThreads;
     if (want > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const unsigned blocks = static_cast<unsigned>(want);
-    const unsigned cap = occupancy_cap_bytes(d, kWgsPerCu);
+    // the dynamic LDS that caps the kernel at kAdamWgsPerCu per CU
     if (L.grad_is_fp16)
-      hipLaunchKernelGGL(adam_vec_kernel<true>, dim3(blocks), dim3(kThreads), cap, stream, a);
+      hipLaunchKernelGGL(adam_vec_kernel<true>, dim3(blocks), dim3(kThreads), d.adam_lds[1],
+                         stream, a);
     else
-      hipLaunchKernelGGL(adam_vec_kernel<false>, dim3(blocks), dim3(kThreads), cap, stream, a);
+      hipLaunchKernelGGL(adam_vec_kernel<false>, dim3(blocks), dim3(kThreads), d.adam_lds[0],
+                         stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -47,27 +47,39 @@ struct GatherLaunch {
 // instead of one copy per shard piece.
 constexpr uint64_t kMaxGatherPieces = 16;
 
-// The device a launch runs on.
-struct DeviceInfo {
-  int cus;         // compute units
-  int lds_per_cu;  // LDS bytes per compute unit
+// Workgroup size and the cap on resident workgroups per compute unit of the
+// two streaming kernels.  The cap is set with dynamic LDS that the kernels do
+// not use: fewer concurrent access streams per CU move more bytes per second
+// on MI355X.  Measured in one process over true residencies 4 to 32 per CU:
+// the reduce (Nd = 64, 25M columns) peaks at 8 (6.47-6.50 TB/s, against 6.06
+// uncapped and 6.36-6.39 at 9); Adam (117M elements) peaks at 10 (6.63 TB/s
+// with an fp32 gradient and 6.55 with fp16, against 6.12 uncapped and
+// 6.54-6.56 / 6.40-6.42 at 9).
+constexpr int kReduceThreads = 64;
+constexpr int kReduceWgsPerCu = 8;
+constexpr int kAdamThreads = 64;
+constexpr int kAdamWgsPerCu = 10;
+
+// The reduce instantiations, by the byte width of their row loads.
+constexpr int kReduceWidths[4] = {16, 8, 4, 2};
+
+// Entry points of the capped kernels, for the occupancy calculator.
+const void* reduce_kernel_fn(int width);       // width: 16, 8, 4 or 2
+const void* adam_kernel_fn(int grad_is_fp16);  // 0 or 1
+
+// What the launches on one device use: its compute-unit count, and for each
+// capped kernel the dynamic LDS bytes that leave exactly its cap of workgroups
+// resident per CU (resolved with the runtime's occupancy calculator on the
+// kernel itself, once per device).
+struct DeviceCaps {
+  int cus;
+  unsigned reduce_lds[4];  // by kReduceWidths
+  unsigned adam_lds[2];    // fp32 gradient, fp16 gradient
 };
 
-// Dynamic LDS bytes per workgroup that let at most `wgs` workgroups share a
-// compute unit.  The kernels do not use this memory: it caps how many
-// workgroups (and so how many concurrent access streams) each CU runs, which
-// on MI355X raises the HBM rate of these streaming kernels (measured: the
-// reduce 6.1 -> 6.5 TB/s at 8 per CU, Adam 6.0 -> 6.55 TB/s at 10).
-inline unsigned occupancy_cap_bytes(const DeviceInfo& d, int wgs) {
-  const unsigned b = static_cast<unsigned>(d.lds_per_cu) / static_cast<unsigned>(wgs);
-  const unsigned granule = 512;
-  const unsigned capped = b > 65536 ? 65536 : b;
-  return (capped / granule) * granule;
-}
-
 // All return hipSuccess or the launch error.
-hipError_t launch_reduce(const ReduceLaunch& a, const DeviceInfo& d, hipStream_t stream);
-hipError_t launch_adam(const AdamLaunch& a, const DeviceInfo& d, hipStream_t stream);
+hipError_t launch_reduce(const ReduceLaunch& a, const DeviceCaps& d, hipStream_t stream);
+hipError_t launch_adam(const AdamLaunch& a, const DeviceCaps& d, hipStream_t stream);
 hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 
 }  // namespace zero

@@ -37,10 +37,9 @@
 namespace zero {
 namespace {
 
-constexpr int kThreads = 64;  // one wavefront per workgroup
-constexpr int kCols = 8;      // columns per thread (one 16-byte fp16 load per row)
-constexpr int kBatch = 16;    // rows per batch
-constexpr int kWgsPerCu = 8;  // occupancy cap
+constexpr int kThreads = kReduceThreads;  // one wavefront per workgroup
+constexpr int kCols = 8;                  // columns per thread (one 16-byte fp16 load per row)
+constexpr int kBatch = 16;                // rows per batch
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -211,7 +210,16 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
 
 }  // namespace
 
-hipError_t launch_reduce(const ReduceLaunch& L, const DeviceInfo& d, hipStream_t stream) {
+const void* reduce_kernel_fn(int width) {
+  switch (width) {
+    case 16: return reinterpret_cast<const void*>(&reduce_kernel<16>);
+    case 8: return reinterpret_cast<const void*>(&reduce_kernel<8>);
+    case 4: return reinterpret_cast<const void*>(&reduce_kernel<4>);
+    default: return reinterpret_cast<const void*>(&reduce_kernel<2>);
+  }
+}
+
+hipError_t launch_reduce(const ReduceLaunch& L, const DeviceCaps& d, hipStream_t stream) {
   Args a;
   a.rows = L.rows;
   a.stride = L.stride;
@@ -244,12 +252,20 @@ hipError_t launch_reduce(const ReduceLaunch& L, const DeviceInfo& d, hipStream_t
   const uint64_t blocks = (a.ngroups + kThreads - 1) / kThreads;
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
-  const unsigned cap = occupancy_cap_bytes(d, kWgsPerCu);
+  // the dynamic LDS that caps each instantiation at kReduceWgsPerCu per CU
   switch (w) {
-    case 16: hipLaunchKernelGGL(reduce_kernel<16>, grid, dim3(kThreads), cap, stream, a); break;
-    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(kThreads), cap, stream, a); break;
-    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(kThreads), cap, stream, a); break;
-    default: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(kThreads), cap, stream, a); break;
+    case 16:
+      hipLaunchKernelGGL(reduce_kernel<16>, grid, dim3(kThreads), d.reduce_lds[0], stream, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(kThreads), d.reduce_lds[1], stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(kThreads), d.reduce_lds[2], stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(kThreads), d.reduce_lds[3], stream, a);
+      break;
   }
   return hipGetLastError();
 }
