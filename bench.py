@@ -119,43 +119,15 @@ def main():
     setup_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     setup_ev[0].record(stream)
     with torch.cuda.stream(stream):
-        master = torch.empty(S, dtype=torch.float32, device=dev)
-        m = torch.empty_like(master)
-        v = torch.empty_like(master)
-        sdev.fill_state(master, w.seed, gen.KIND_MASTER, lo, w.master.sigma)
-        sdev.fill_state(m, w.seed, gen.KIND_M, lo, w.m.sigma, w.m.absolute)
-        sdev.fill_state(v, w.seed, gen.KIND_V, lo, w.v.sigma, w.v.absolute)
-        if stage3:
-            # every rank's fp16 parameter shard (the all-gather sources); row
-            # `rank` is this rank's own shard, which its Adam step writes
-            s_all = -(-w.psi // w.nd)
-            shards = torch.empty((w.nd, s_all), dtype=torch.int16, device=dev)
-            for k in range(w.nd):
-                k_lo = min(k * s_all, w.psi)
-                k_n = min((k + 1) * s_all, w.psi) - k_lo
-                if k_n:
-                    sdev.fill_grad_rows(shards[k:k + 1, :k_n], w.seed, k_lo,
-                                        w.extra["param_sigma"], rank0=k, kind=gen.KIND_PARAM16)
-            param16, param16_origin = shards[w.rank, :S], lo
-            layer_buf = torch.empty(max(n for _, n in w.buckets), dtype=torch.int16, device=dev)
-        elif "p16_window" in w.extra:
-            # the rank's slot and a margin either side of it, at its place in the
-            # flat fp16 vector (the whole vector does not fit beside the rows)
-            win = w.extra["p16_window"]
-            param16_origin = max(0, lo - win)
-            param16 = torch.zeros(min(w.psi, lo + S + win) - param16_origin, dtype=torch.int16,
-                                  device=dev)
-        else:
-            param16, param16_origin = torch.zeros(w.psi, dtype=torch.int16, device=dev), 0
+        # The reduce's rows are allocated first.  On MI355X the rate at which a
+        # row buffer reads (and so the reduce, at 0.88-0.89 of it) depends on
+        # where the allocation lands: 7.1 or 6.9 TB/s for the same rows.  The
+        # order of allocation does not decide it -- over 17 processes on two
+        # boxes, rows first, rows last and one pooled buffer each landed either
+        # way, and the box's first process mostly landed fast.
         buckets = []          # (flat offset, length, rows) per reduce launch
         n_buckets = 0         # buckets meeting the shard
-        if w.fp16_grad:
-            grad = torch.empty(S, dtype=torch.int16, device=dev)
-            sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
-                                kind=gen.KIND_GRAD_FULL)
-        else:
-            g16 = w.grad_shard == "fp16"
-            grad = torch.zeros(S, dtype=torch.int16 if g16 else torch.float32, device=dev)
+        if not w.fp16_grad:
             chunk = w.extra.get("chunk")          # rows arrive in column chunks
             for off, n in wl.buckets_touching(w.buckets, lo, lo + S):
                 a, b = Z.bucket_intersect(geom, off, n)
@@ -167,13 +139,53 @@ def main():
                     rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
                     sdev.fill_grad_rows(rows, w.seed, c0, w.grad.sigma, w.grad.heavy_tail)
                     buckets.append((c0, c1 - c0, rows))
+        if stage3:
+            # every rank's fp16 parameter shard (the all-gather sources); row
+            # `rank` is this rank's own shard, which its Adam step writes
+            s_all = -(-w.psi // w.nd)
+            shards = torch.empty((w.nd, s_all), dtype=torch.int16, device=dev)
+            fill_param_shards(sdev, gen, w, shards)
+            param16, param16_origin = shards[w.rank, :S], lo
+            layer_buf = torch.empty(max(n for _, n in w.buckets), dtype=torch.int16, device=dev)
+        live = RankArrays(torch, dev, S)
+        live.fill_initial(sdev, gen, w, lo)
+        if w.fp16_grad:
+            grad = torch.empty(S, dtype=torch.int16, device=dev)
+            sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
+                                kind=gen.KIND_GRAD_FULL)
+        else:
+            grad = torch.zeros(S, dtype=torch.int16 if w.grad_shard == "fp16" else torch.float32,
+                               device=dev)
+        if stage3:
+            pass                                  # the slot is the own parameter shard
+        elif "p16_window" in w.extra:
+            # the rank's slot and a margin either side of it, at its place in the
+            # flat fp16 vector (the whole vector does not fit beside the rows)
+            win = w.extra["p16_window"]
+            param16_origin = max(0, lo - win)
+            param16 = torch.zeros(min(w.psi, lo + S + win) - param16_origin, dtype=torch.int16,
+                                  device=dev)
+        else:
+            param16, param16_origin = torch.zeros(w.psi, dtype=torch.int16, device=dev), 0
+        live.set_slot(param16, param16_origin)
+        # Scratch state for the warm-up steps and for timed steps beyond the
+        # workload's own count: Adam updates in place, so those steps run on
+        # copies and the live state follows exactly the workload's trajectory
+        # t = 1..K.  The scratch fp16 slot sits at the live slot's address
+        # modulo 256 bytes, so both take the same store widths.
+        scratch = RankArrays(torch, dev, S)
+        scratch.copy_from(live)
+        slot_ptr = param16.data_ptr() + 2 * (lo - param16_origin)
+        sbuf = torch.empty(S + 128, dtype=torch.int16, device=dev)
+        e = ((slot_ptr - sbuf.data_ptr()) % 256) // 2
+        scratch.set_slot(sbuf[e:e + S], lo)
     setup_ev[1].record(stream)
     torch.cuda.synchronize()
     input_setup = {"wall_s": time.perf_counter() - setup_wall0,
                    "device_ms": setup_ev[0].elapsed_time(setup_ev[1]),
                    "bytes_resident": torch.cuda.memory_allocated(),
                    "what": "seeded synthetic inputs generated on the device (untimed, not in "
-                           "value)"}
+                           "value); gradient rows allocated first, then the model state"}
     init_idx = None
     if args.check_samples:
         rng = np.random.default_rng(1)
@@ -200,7 +212,8 @@ def main():
     g_bytes = 4 if grad.dtype == torch.float32 else 2
     red_of = {a: rows for a, _, rows in buckets}
 
-    def launches(t):
+    def launches(t, st):
+        """The launches of step t on the rank arrays `st` (live or scratch)."""
         ops = []
 
         def reduce_op(a, n, rows):
@@ -224,11 +237,9 @@ def main():
             for a, n, rows in buckets:
                 ops.append(("reduce", n * (2 * w.nd + g_bytes), reduce_op(a, n, rows)))
         ops.append(("adam", S * (26 + g_bytes), lambda: Z.adam_step_shard(
-            geom, master, m, v, grad, param16, param16_origin, w.lr, w.beta1, w.beta2, w.eps,
-            t, stream=stream)))
+            geom, st.master, st.m, st.v, grad, st.p16, st.p16_origin, w.lr, w.beta1, w.beta2,
+            w.eps, t, stream=stream)))
         return ops
-
-    t_counter = [0]
 
     def runs_of(ops):
         """Consecutive launches of one kernel kind: [(kind, launches), ...]."""
@@ -240,11 +251,10 @@ def main():
                 runs.append([kind, 1])
         return runs
 
-    def step(events=None):
-        """One step; with events, one is recorded before each run of launches of
-        one kind and one after the step's last launch."""
-        t_counter[0] += 1
-        ops = launches(t_counter[0])
+    def step(t, st, events=None):
+        """Step t on `st`; with events, one is recorded before each run of
+        launches of one kind and one after the step's last launch."""
+        ops = launches(t, st)
         prev, r = None, 0
         for kind, _, fn in ops:
             if events is not None and kind != prev:
@@ -262,21 +272,31 @@ def main():
     # the timed steps: a full collection takes tens of milliseconds on the host,
     # and one falling between two timed steps left the GPU idle for as long once
     # the launches already queued had drained.
+    # The live state takes steps t = 1..K of the workload (K = its own step
+    # count, or fewer when fewer steps are timed); warm-ups and timed steps past
+    # K run on the scratch copy, which continues its own count.
+    k_live = min(args.steps, w.steps)
+    t_scratch = 0
     gc.collect()
     gc.disable()
     for _ in range(args.warmup):
-        step()
+        t_scratch += 1
+        step(t_scratch, scratch)
     torch.cuda.synchronize()
     # The timed steps: besides the path's own launches the stream holds only the
     # events at the boundaries of each run of one kernel kind (3 per step for
     # stage 2), so the per-kernel figures come from the timed region itself.
-    runs = runs_of(launches(1))
+    runs = runs_of(launches(1, live))
     per_step = [[ev() for _ in range(len(runs) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ops = None
     for k in range(args.steps):
-        ops = step(per_step[k])
+        if k < k_live:
+            ops = step(k + 1, live, per_step[k])
+        else:
+            t_scratch += 1
+            ops = step(t_scratch, scratch, per_step[k])
     enqueued = time.perf_counter() - wall0         # host time to issue the timed steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -315,11 +335,10 @@ def main():
     # ---- sampled self-check against the oracle (untimed) --------------------------------
     parity = None
     if init_idx is not None:
-        parity = self_check(w, geom, buckets, grad, master, m, v, param16, param16_origin,
-                            init_idx, t_counter[0])
+        parity = self_check(w, geom, buckets, grad, live.master, live.m, live.v, param16,
+                            param16_origin, init_idx, k_live)
         if stage3:
-            parity.update(gather_check(w, geom, shards, layer_buf, init_idx, t_counter[0],
-                                       stream))
+            parity.update(gather_check(w, geom, shards, layer_buf, init_idx, k_live, stream))
 
     ceilings = None
     if not args.no_ceilings:
@@ -344,7 +363,7 @@ def main():
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "fp16-io/fp32-state", "data": "synthetic",
         "hbm_gbs": gbs(step_bytes, ms_step),
         "hbm_frac_of_peak": gbs(step_bytes, ms_step) / PEAK_HBM_GBS,
         "bytes_per_step": step_bytes,
@@ -362,6 +381,11 @@ def main():
                    "slot": ("own fp16 shard" if stage3 else
                             "fp16 flat vector window" if "p16_window" in w.extra else
                             "fp16 flat vector")},
+        "trajectory": {"live_steps": k_live, "workload_steps": w.steps,
+                       "scratch_steps": args.warmup + args.steps - k_live,
+                       "what": "the live state takes steps t = 1..live_steps; warm-ups and "
+                               "timed steps past the workload's count run on a scratch copy "
+                               "of master/m/v and of the fp16 slot"},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -371,6 +395,39 @@ def main():
         "env": environment(torch, dev),
     }
     print(json.dumps(out), flush=True)
+
+
+class RankArrays:
+    """The rank's Adam state (fp32 master, m, v) and the fp16 slot its step writes."""
+
+    def __init__(self, torch, dev, n):
+        self.master = torch.empty(n, dtype=torch.float32, device=dev)
+        self.m = torch.empty_like(self.master)
+        self.v = torch.empty_like(self.master)
+        self.p16, self.p16_origin = None, 0
+
+    def fill_initial(self, sdev, gen, w, lo):
+        sdev.fill_state(self.master, w.seed, gen.KIND_MASTER, lo, w.master.sigma)
+        sdev.fill_state(self.m, w.seed, gen.KIND_M, lo, w.m.sigma, w.m.absolute)
+        sdev.fill_state(self.v, w.seed, gen.KIND_V, lo, w.v.sigma, w.v.absolute)
+
+    def copy_from(self, other):
+        for a, b in ((self.master, other.master), (self.m, other.m), (self.v, other.v)):
+            a.copy_(b)
+
+    def set_slot(self, p16, origin):
+        self.p16, self.p16_origin = p16, origin
+
+
+def fill_param_shards(sdev, gen, w, shards):
+    """Stage 3: every rank's fp16 parameter shard, row k = rank k's."""
+    s_all = shards.shape[1]
+    for k in range(w.nd):
+        k_lo = min(k * s_all, w.psi)
+        k_n = min((k + 1) * s_all, w.psi) - k_lo
+        if k_n:
+            sdev.fill_grad_rows(shards[k:k + 1, :k_n], w.seed, k_lo, w.extra["param_sigma"],
+                                rank0=k, kind=gen.KIND_PARAM16)
 
 
 def stream_ceilings(torch, dev, stream, rows=None, nbytes=4 << 30, reps=10):
