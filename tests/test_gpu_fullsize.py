@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import zero_sharded_mixed_bucketed_amd as Z
+import oracle_pool
 from gpu_util import assert_adam_step, assert_bits, gather, need_gpu, sample_indices
 from oracle import adam as oadam
 from oracle import reduce as ored
@@ -49,7 +50,9 @@ def _host_state(w, flat):
 
 def _reduce_all(w, geom, grad32, chunk=None):
     """Every bucket that meets the shard, in arrival order; only the owned columns
-    arrive (rows at the library's advised stride); the rows are freed after each call."""
+    arrive (rows at the library's advised stride); the rows are freed after each call.
+    Returns the shard-local edges of every bucket and of every chunk launch (each
+    chunk is a row buffer of its own and starts a new output alignment class)."""
     edges = []
     for off, n in wl.buckets_touching(w.buckets, geom.offset, geom.offset + geom.len):
         a, b = Z.bucket_intersect(geom, off, n)
@@ -57,6 +60,7 @@ def _reduce_all(w, geom, grad32, chunk=None):
         step = chunk or (b - a)
         for c0 in range(a, b, step):
             c1 = min(b, c0 + step)
+            edges.append(c0 - geom.offset)
             stride = Z.row_stride(c1 - c0)
             buf = torch.empty(w.nd * stride, dtype=torch.int16, device="cuda")
             rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
@@ -120,6 +124,71 @@ def _run_zero2(w, chunk=None, window=None):
 def test_fullsize_zero2_7p5b_rank0():
     """7.5B at Nd = 64, rank 0: five buckets (17,187,500 + 4 x 25M), 10 steps."""
     _run_zero2(wl.zero2_7p5b(0))
+
+
+@pytest.mark.timeout(900)
+def test_fullstate_zero2_7p5b_rank0():
+    """Every element, not a sample, at the 7.5B / Nd = 64 rank 0 shard
+    (117,187,500 elements), in the bench's launch configuration: the reduced
+    fp32 gradient after the reduce pass over the five buckets, and master, m, v
+    and the fp16 slot after each of the 10 Adam steps.  The oracle runs over the
+    whole shard in 2^22-element chunks in a spawn pool (tests/oracle_pool.py)
+    while the device works, and returns per-chunk SHA-256 digests; the device
+    results are hashed the same way.  A chunk whose digests differ is compared
+    element by element under the bars of tests/gpu_util.py, from the device
+    state before that step, so a failure names the elements."""
+    w = wl.zero2_7p5b(0)
+    geom = Z.shard_geometry(w.psi, w.nd, w.rank)
+    lo, S = geom.offset, geom.len
+    print(f"{w.name}: full state over [{lo}, +{S}), oracle on {oracle_pool.workers()} "
+          f"processes", flush=True)
+    orc = oracle_pool.ShardOracle(w, lo, S, w.steps)
+    try:
+        state = _state(w, geom)
+        grad32 = torch.zeros(S, dtype=torch.float32, device="cuda")
+        _reduce_all(w, geom, grad32)
+        p16 = torch.zeros(w.psi, dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        spans = orc.chunks
+        dev = {("grad32", 0): oracle_pool.chunk_digests(grad32.cpu().numpy(), spans)}
+        snaps = [[x.clone() for x in state]]            # device state before each step
+        for t in range(1, w.steps + 1):
+            Z.adam_step_shard(geom, *state, grad32, p16, 0, w.lr, w.beta1, w.beta2, w.eps, t)
+            torch.cuda.synchronize()
+            host = [x.cpu().numpy() for x in state]
+            host.append(p16[lo:lo + S].cpu().numpy().view(np.uint16))
+            for name, a in zip(oracle_pool.ARRAYS, host):
+                dev[(name, t)] = oracle_pool.chunk_digests(a, spans)
+            snaps.append([x.clone() for x in state] + [p16[lo:lo + S].clone()])
+            del host
+            print(f"step {t} hashed", flush=True)
+        # nothing outside the slot was written
+        assert torch.count_nonzero(p16[lo + S:]).item() == 0
+        want = orc.result()
+    finally:
+        orc.close()
+    # earliest step first: a difference carries over into the later steps
+    bad = [(key, j0) for key in sorted(want, key=lambda k: (k[1], k[0]))
+           for j0, h in sorted(want[key].items()) if dev[key][j0] != h]
+    compared = sum(len(v) for v in want.values())
+    print(f"{compared} chunk digests compared, {len(bad)} differ", flush=True)
+    assert compared == len(spans) * (1 + len(oracle_pool.ARRAYS) * w.steps)
+    assert all(set(dev[key]) == set(want[key]) for key in want)
+    if bad:
+        (name, t), j0 = bad[0]
+        n = dict(spans)[j0]
+        flat = np.arange(lo + j0, lo + j0 + n, dtype=np.uint64)
+        g_ref = _oracle_grad(w, flat)
+        assert_bits(grad32[j0:j0 + n].cpu().numpy(), g_ref, f"reduced gradient, chunk {j0}")
+        before = [x[j0:j0 + n].cpu().numpy() for x in snaps[t - 1][:3]]
+        after = [x[j0:j0 + n].cpu().numpy() for x in snaps[t][:3]]
+        got_p = snaps[t][3][j0:j0 + n].cpu().numpy().view(np.uint16)
+        sc = oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, t)
+        assert_adam_step((*before, oadam.grad_f32(g_ref)), (*after, got_p),
+                         oadam.step_values(*before, g_ref, sc), c1=float(sc.c1),
+                         b1=float(sc.b1), b2=float(sc.b2), c2=float(sc.c2),
+                         what=f"step {t}, chunk {j0}")
+        pytest.fail(f"digests differ at {bad[:8]}")
 
 
 def test_fullsize_zero2_7p5b_rank1():
