@@ -7,8 +7,8 @@ Sources:
   process that needs another's partition receives it; memory falls to
   16 Psi / Nd; communication is two parameter all-gathers (forward and
   backward) plus the gradient reduce-scatter.
-* lastdictionary entry "ZeRO": stage 3 gathers each layer's parameters just
-  in time for computation and discards them afterwards.
+* lastdictionary entry "ZeRO": in stage 3 a layer's parameters are fetched
+  right before that layer runs and dropped once it is done.
 * llm-engineer card "ZeRO-2", section "Why all-gather is still needed": the
   all-gather of the rank partitions, in rank order, is the full vector
   [A, B, C].

@@ -50,11 +50,13 @@ def _shards_host(psi, nd, width, seed):
     (1_000_003, 7, 1, 142_858, 142_857, 1),     # rows 2 bytes apart: 2-byte copies
     (1_000_003, 7, 2, 3, 500_000, 2),           # 4-byte relative alignment
     (1_000_003, 7, 4, 3, 500_000, 0),           # 8-byte relative alignment
-    (600, 200, 0, 5, 590, 0),                   # many small shards: element-wise kernel
-    (1_700, 100, 0, 0, 272, 0),                 # exactly 16 whole shards: one piece each
-    (1_700, 100, 0, 0, 273, 0),                 # 17 pieces: the element-wise kernel
+    (600, 200, 0, 5, 590, 0),                   # many small shards: 13 launches of <= 16 pieces
+    (1_700, 100, 0, 0, 272, 0),                 # exactly 16 whole shards: one launch
+    (1_700, 100, 0, 0, 273, 0),                 # 17 pieces: a second launch of one piece
     (1_700, 100, 3, 5, 267, 1),                 # 16 pieces, ragged at both ends
     (1_700, 100, 3, 5, 268, 1),                 # 17 pieces, ragged at both ends
+    (3_300_000, 33, 11, 99_990, 3_000_000, 5),  # 31 pieces of 100,000, lines off by 22 bytes
+    (1_000_003, 7, 0, 1_000, 20, 0),            # shorter than the head to the next line
     (10, 3, 0, 9, 1, 1),                        # the last element (short last shard)
 ])
 def test_gather_matches_oracle(psi, nd, pad, lo, n, out_shift):

@@ -43,8 +43,8 @@ struct GatherLaunch {
   uint16_t* out;
 };
 
-// A gather crossing more rank shards than this runs as one element-wise launch
-// instead of one copy per shard piece.
+// Pieces (rank shards crossed) per gather launch; a gather that crosses more
+// shards takes several launches.
 constexpr uint64_t kMaxGatherPieces = 16;
 
 // Workgroup size and the cap on resident workgroups per compute unit of the
