@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--check-samples", type=int, default=4096)
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the streaming ceilings reported for context")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the wait for a quiet device before the warm-up steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (untimed) so that a counter "
                          "profile of this run holds a kernel of known traffic")
@@ -119,12 +121,8 @@ def main():
     setup_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     setup_ev[0].record(stream)
     with torch.cuda.stream(stream):
-        # The reduce's rows are allocated first.  On MI355X the rate at which a
-        # row buffer reads (and so the reduce, at 0.88-0.89 of it) depends on
-        # where the allocation lands: 7.1 or 6.9 TB/s for the same rows.  The
-        # order of allocation does not decide it -- over 17 processes on two
-        # boxes, rows first, rows last and one pooled buffer each landed either
-        # way, and the box's first process mostly landed fast.
+        # The reduce's rows are allocated first (the order does not change how
+        # fast they read once the device is quiet; see the settle step below).
         buckets = []          # (flat offset, length, rows) per reduce launch
         n_buckets = 0         # buckets meeting the shard
         if not w.fp16_grad:
@@ -268,6 +266,15 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # Wait for a quiet device.  The driver clears freed device memory in the
+    # background: after a process frees tens of GB (the previous run's exit
+    # does), concurrent kernels stream 1-5% slower for a few seconds.  Before
+    # the warm-ups, a read of the workload's own resident data is repeated
+    # until its rate has not risen for a second.
+    settle = None if args.no_settle else settle_device(
+        torch, stream, buckets[max(range(len(buckets)), key=lambda i: buckets[i][1])][2]
+        if buckets else grad.view(1, -1))
+
     # Python's cyclic garbage collector stays off from the warm-up to the end of
     # the timed steps: a full collection takes tens of milliseconds on the host,
     # and one falling between two timed steps left the GPU idle for as long once
@@ -392,6 +399,7 @@ def main():
         "parity": parity,
         "ceilings": ceilings,
         "input_setup": input_setup,
+        "device_settle": settle,
         "env": environment(torch, dev),
     }
     print(json.dumps(out), flush=True)
@@ -428,6 +436,40 @@ def fill_param_shards(sdev, gen, w, shards):
         if k_n:
             sdev.fill_grad_rows(shards[k:k + 1, :k_n], w.seed, k_lo, w.extra["param_sigma"],
                                 rank0=k, kind=gen.KIND_PARAM16)
+
+
+def settle_device(torch, stream, rows, quiet_s=1.0, max_s=12.0, period_s=0.1):
+    """Repeat a read of `rows` (a [n, cols] int16 view, the workload's own resident
+    data) until its rate has not risen by more than 0.3% for `quiet_s` seconds,
+    or for at most `max_s`.  Returns the wait and the first and best rates."""
+    from synth import probe
+    cols = rows.shape[1] // 8 * 8
+    view = rows[:, :cols]
+    with torch.cuda.stream(stream):
+        sink = torch.zeros(1, dtype=torch.int32, device=rows.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    nbytes = 2 * view.shape[0] * cols
+    t0 = time.perf_counter()
+    rates, best, t_best = [], 0.0, t0
+    while True:
+        with torch.cuda.stream(stream):
+            ev[0].record(stream)
+            for _ in range(3):
+                probe.read_rows(view, sink, 8, stream=stream)
+            ev[1].record(stream)
+        torch.cuda.synchronize()
+        r = 3 * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+        rates.append(r)
+        now = time.perf_counter()
+        if r > best * 1.003:
+            best, t_best = r, now
+        if now - t_best >= quiet_s or now - t0 >= max_s:
+            break
+        time.sleep(period_s)
+    return {"seconds": time.perf_counter() - t0, "reads": len(rates), "first_gbs": rates[0],
+            "best_gbs": best, "what": "untimed reads of the workload's resident data before the "
+                                      "warm-ups, until the rate stops rising (the driver clears "
+                                      "freed device memory in the background)"}
 
 
 def stream_ceilings(torch, dev, stream, rows=None, nbytes=4 << 30, reps=10):

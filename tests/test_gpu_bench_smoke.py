@@ -44,3 +44,5 @@ def test_bench_tiny_prints_one_contract_line():
     tr = d["trajectory"]
     assert (tr["live_steps"], tr["workload_steps"], tr["scratch_steps"]) == (3, 3, 3)
     assert d["dtype"] == "fp16-io/fp32-state"
+    st = d["device_settle"]                  # the wait for a quiet device ran first
+    assert st["reads"] >= 2 and 1.0 <= st["seconds"] < 20.0 and st["best_gbs"] > 0
