@@ -36,29 +36,43 @@ def workers() -> int:
 
 
 def chunk_inputs(w, flat):
-    """The seeded inputs at flat indices: the Nd fp16 rows and the initial state."""
+    """The seeded inputs at flat indices: the Nd fp16 rows (for plain data
+    parallelism, the one raw fp16 gradient) and the initial state."""
     from synth import gen
-    rows = np.empty((w.nd, flat.size), np.uint16)
-    for k in range(w.nd):
-        rows[k] = gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
+    if w.fp16_grad:
+        rows = gen.grad_f16(w.seed, 0, flat, w.grad.sigma, w.grad.heavy_tail,
+                            kind=gen.KIND_GRAD_FULL)[None, :]
+    else:
+        rows = np.empty((w.nd, flat.size), np.uint16)
+        for k in range(w.nd):
+            rows[k] = gen.grad_f16(w.seed, k, flat, w.grad.sigma, w.grad.heavy_tail)
     state = (gen.state_f32(w.seed, gen.KIND_MASTER, flat, w.master.sigma),
              gen.state_f32(w.seed, gen.KIND_M, flat, w.m.sigma, w.m.absolute),
              gen.state_f32(w.seed, gen.KIND_V, flat, w.v.sigma, w.v.absolute))
     return rows, state
 
 
-def chunk_trajectory(job):
-    """In a worker: digests of the oracle's reduced gradient (key ("grad32", 0))
-    and of master, m, v and the fp16 parameters after each step t = 1..steps,
-    for shard-local elements [j0, j0 + n)."""
-    from oracle import adam as oadam
+def chunk_gradient(w, rows):
+    """The gradient Adam reads: the reduced fp32 shard, its fp16 copy for an fp16
+    shard, or the raw fp16 gradient of plain data parallelism."""
     from oracle import reduce as ored
+    if w.fp16_grad:
+        return rows[0]
+    g = ored.reduce_values(rows, w.nd)
+    return g.astype(np.float16).view(np.uint16) if w.grad_shard == "fp16" else g
+
+
+def chunk_trajectory(job):
+    """In a worker: digests of the gradient Adam reads (key ("grad", 0)) and of
+    master, m, v and the fp16 parameters after each step t = 1..steps, for
+    shard-local elements [j0, j0 + n)."""
+    from oracle import adam as oadam
     w, offset, j0, n, steps = job
     flat = np.arange(offset + j0, offset + j0 + n, dtype=np.uint64)
     rows, (th, m, v) = chunk_inputs(w, flat)
-    g = ored.reduce_values(rows, w.nd)
+    g = chunk_gradient(w, rows)
     del rows
-    out = {("grad32", 0): digest(g)}
+    out = {("grad", 0): digest(g)}
     for t in range(1, steps + 1):
         th, m, v, p16 = oadam.step_values(th, m, v, g,
                                           oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, t))

@@ -126,69 +126,111 @@ def test_fullsize_zero2_7p5b_rank0():
     _run_zero2(wl.zero2_7p5b(0))
 
 
-@pytest.mark.timeout(900)
-def test_fullstate_zero2_7p5b_rank0():
-    """Every element, not a sample, at the 7.5B / Nd = 64 rank 0 shard
-    (117,187,500 elements), in the bench's launch configuration: the reduced
-    fp32 gradient after the reduce pass over the five buckets, and master, m, v
-    and the fp16 slot after each of the 10 Adam steps.  The oracle runs over the
-    whole shard in 2^22-element chunks in a spawn pool (tests/oracle_pool.py)
-    while the device works, and returns per-chunk SHA-256 digests; the device
-    results are hashed the same way.  A chunk whose digests differ is compared
-    element by element under the bars of tests/gpu_util.py, from the device
-    state before that step, so a failure names the elements."""
-    w = wl.zero2_7p5b(0)
+def _fullstate(w):
+    """Every element, not a sample, of one rank's shard in the bench's launch
+    configuration: the gradient Adam reads (the reduced fp32 shard after the
+    reduce pass over all buckets, or plain data parallelism's raw fp16
+    gradient), then master, m, v and the fp16 slot after each of the
+    workload's Adam steps.  The oracle runs over the whole shard in
+    2^22-element chunks in a spawn pool (tests/oracle_pool.py) while the device
+    works, and returns per-chunk SHA-256 digests; the device results are hashed
+    the same way after each step.  A chunk that differs is compared element by
+    element under the bars of tests/gpu_util.py, from the device state before
+    that step (kept as one snapshot), so a failure names the elements."""
     geom = Z.shard_geometry(w.psi, w.nd, w.rank)
     lo, S = geom.offset, geom.len
-    print(f"{w.name}: full state over [{lo}, +{S}), oracle on {oracle_pool.workers()} "
-          f"processes", flush=True)
+    print(f"{w.name}: full state over [{lo}, +{S}), {w.steps} steps, oracle on "
+          f"{oracle_pool.workers()} processes", flush=True)
     orc = oracle_pool.ShardOracle(w, lo, S, w.steps)
     try:
         state = _state(w, geom)
-        grad32 = torch.zeros(S, dtype=torch.float32, device="cuda")
-        _reduce_all(w, geom, grad32)
+        if w.fp16_grad:
+            grad = torch.empty(S, dtype=torch.int16, device="cuda")
+            sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
+                                kind=gen.KIND_GRAD_FULL)
+        else:
+            grad = torch.zeros(S, dtype=torch.float32, device="cuda")
+            _reduce_all(w, geom, grad)
         p16 = torch.zeros(w.psi, dtype=torch.int16, device="cuda")
         torch.cuda.synchronize()
         spans = orc.chunks
-        dev = {("grad32", 0): oracle_pool.chunk_digests(grad32.cpu().numpy(), spans)}
-        snaps = [[x.clone() for x in state]]            # device state before each step
-        for t in range(1, w.steps + 1):
-            Z.adam_step_shard(geom, *state, grad32, p16, 0, w.lr, w.beta1, w.beta2, w.eps, t)
-            torch.cuda.synchronize()
-            host = [x.cpu().numpy() for x in state]
-            host.append(p16[lo:lo + S].cpu().numpy().view(np.uint16))
-            for name, a in zip(oracle_pool.ARRAYS, host):
-                dev[(name, t)] = oracle_pool.chunk_digests(a, spans)
-            snaps.append([x.clone() for x in state] + [p16[lo:lo + S].clone()])
-            del host
-            print(f"step {t} hashed", flush=True)
-        # nothing outside the slot was written
-        assert torch.count_nonzero(p16[lo + S:]).item() == 0
+        g_host = grad.cpu().numpy()
+        got_g = oracle_pool.chunk_digests(g_host, spans)
         want = orc.result()
     finally:
         orc.close()
-    # earliest step first: a difference carries over into the later steps
-    bad = [(key, j0) for key in sorted(want, key=lambda k: (k[1], k[0]))
-           for j0, h in sorted(want[key].items()) if dev[key][j0] != h]
-    compared = sum(len(v) for v in want.values())
-    print(f"{compared} chunk digests compared, {len(bad)} differ", flush=True)
-    assert compared == len(spans) * (1 + len(oracle_pool.ARRAYS) * w.steps)
-    assert all(set(dev[key]) == set(want[key]) for key in want)
-    if bad:
-        (name, t), j0 = bad[0]
-        n = dict(spans)[j0]
+    assert set(want) == {("grad", 0)} | {(n, t) for n in oracle_pool.ARRAYS
+                                         for t in range(1, w.steps + 1)}
+
+    def oracle_grad(j0, n):
         flat = np.arange(lo + j0, lo + j0 + n, dtype=np.uint64)
-        g_ref = _oracle_grad(w, flat)
-        assert_bits(grad32[j0:j0 + n].cpu().numpy(), g_ref, f"reduced gradient, chunk {j0}")
-        before = [x[j0:j0 + n].cpu().numpy() for x in snaps[t - 1][:3]]
-        after = [x[j0:j0 + n].cpu().numpy() for x in snaps[t][:3]]
-        got_p = snaps[t][3][j0:j0 + n].cpu().numpy().view(np.uint16)
-        sc = oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, t)
-        assert_adam_step((*before, oadam.grad_f32(g_ref)), (*after, got_p),
-                         oadam.step_values(*before, g_ref, sc), c1=float(sc.c1),
-                         b1=float(sc.b1), b2=float(sc.b2), c2=float(sc.c2),
-                         what=f"step {t}, chunk {j0}")
-        pytest.fail(f"digests differ at {bad[:8]}")
+        if w.fp16_grad:
+            return gen.grad_f16(w.seed, 0, flat, w.grad.sigma, w.grad.heavy_tail,
+                                kind=gen.KIND_GRAD_FULL)
+        return _oracle_grad(w, flat)
+
+    spans_d = dict(spans)
+    bad = [j0 for j0, h in sorted(want[("grad", 0)].items()) if got_g[j0] != h]
+    if bad:
+        j0 = bad[0]
+        assert_bits(g_host[j0:j0 + spans_d[j0]].view(np.uint16 if w.fp16_grad else np.float32),
+                    oracle_grad(j0, spans_d[j0]), f"gradient, chunk {j0}")
+        pytest.fail(f"gradient digests differ at chunks {bad[:8]}")
+    del g_host
+    compared = len(spans)
+    for t in range(1, w.steps + 1):
+        before = [x.clone() for x in state]
+        Z.adam_step_shard(geom, *state, grad, p16, 0, w.lr, w.beta1, w.beta2, w.eps, t)
+        torch.cuda.synchronize()
+        host = [x.cpu().numpy() for x in state]
+        host.append(p16[lo:lo + S].cpu().numpy().view(np.uint16))
+        bad = []
+        for name, a in zip(oracle_pool.ARRAYS, host):
+            d = oracle_pool.chunk_digests(a, spans)
+            bad += [(j0, name) for j0, h in want[(name, t)].items() if d[j0] != h]
+            compared += len(spans)
+        if bad:
+            j0, name = min(bad)
+            n = spans_d[j0]
+            g_ref = oracle_grad(j0, n)
+            prev = [x[j0:j0 + n].cpu().numpy() for x in before]
+            sc = oadam.scalars(w.lr, w.beta1, w.beta2, w.eps, t)
+            assert_adam_step((*prev, oadam.grad_f32(g_ref)),
+                             tuple(a[j0:j0 + n] for a in host),
+                             oadam.step_values(*prev, g_ref, sc), c1=float(sc.c1),
+                             b1=float(sc.b1), b2=float(sc.b2), c2=float(sc.c2),
+                             what=f"step {t}, chunk {j0}")
+            pytest.fail(f"step {t}: digests differ at {sorted(bad)[:8]}")
+        del before, host
+        print(f"step {t}: {4 * len(spans)} chunk digests equal", flush=True)
+    # nothing outside the slot was written
+    assert torch.count_nonzero(p16[:lo]).item() == 0
+    assert torch.count_nonzero(p16[lo + S:]).item() == 0
+    assert compared == len(spans) * (1 + len(oracle_pool.ARRAYS) * w.steps)
+    print(f"{compared} chunk digests compared, all equal", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_fullstate_zero2_7p5b_rank0():
+    """Every element of the 7.5B / Nd = 64 rank-0 shard (117,187,500): the reduced
+    fp32 gradient over the five buckets and the state after each of 10 steps."""
+    _fullstate(wl.zero2_7p5b(0))
+
+
+@pytest.mark.timeout(900)
+def test_fullstate_zero2_13b_rank0():
+    """Every element of the 13B / Nd = 32 rank-0 shard (406,250,000) with
+    heavy-tailed gradients (exact zeros and x100 outliers, so partial sums leave
+    the exact range): the reduced fp32 gradient over 17 buckets and the state
+    after each of 10 steps."""
+    _fullstate(wl.zero2_13b(0))
+
+
+@pytest.mark.timeout(900)
+def test_fullstate_plain_dp_1p4b():
+    """Every element of plain data parallelism at 1.4B (Nd = 1, no reduce): the
+    fused Adam on the raw fp16 gradient, each of 20 steps."""
+    _fullstate(wl.plain_dp_1p4b())
 
 
 def test_fullsize_zero2_7p5b_rank1():

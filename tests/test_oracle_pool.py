@@ -18,10 +18,10 @@ def test_pool_digests_equal_a_direct_oracle_run():
     orc = oracle_pool.ShardOracle(w, lo, S, w.steps, chunk=chunk)
     want = orc.result(timeout=600)
     spans = oracle_pool.chunks(S, chunk)
-    assert len(spans) == 4 and sorted(want[("grad32", 0)]) == [j0 for j0, _ in spans]
+    assert len(spans) == 4 and sorted(want[("grad", 0)]) == [j0 for j0, _ in spans]
     flat = np.arange(lo, lo + S, dtype=np.uint64)
     g = ored.reduce_values(gen.grad_rows(w.seed, w.nd, lo, lo + S, w.grad.sigma), w.nd)
-    assert oracle_pool.chunk_digests(g, spans) == want[("grad32", 0)]
+    assert oracle_pool.chunk_digests(g, spans) == want[("grad", 0)]
     th = gen.state_f32(w.seed, gen.KIND_MASTER, flat, w.master.sigma)
     m = np.zeros(S, np.float32)
     v = np.zeros(S, np.float32)
@@ -35,3 +35,21 @@ def test_pool_digests_equal_a_direct_oracle_run():
     th2.view(np.uint32)[3 * chunk + 5] ^= 1
     d2 = oracle_pool.chunk_digests(th2, spans)
     assert [j0 for j0, _ in spans if d2[j0] != want[("master", w.steps)][j0]] == [3 * chunk]
+
+
+def test_pool_fp16_gradients():
+    """The raw fp16 gradient of plain data parallelism and an fp16 gradient shard
+    are what the pool's chunks digest."""
+    from dataclasses import replace
+    base = wl.tiny()
+    flat = np.arange(0, 1 << 12, dtype=np.uint64)
+    plain = replace(base, nd=1, fp16_grad=True, steps=1)
+    rows, _ = oracle_pool.chunk_inputs(plain, flat)
+    g = oracle_pool.chunk_gradient(plain, rows)
+    assert g.dtype == np.uint16 and np.array_equal(
+        g, gen.grad_f16(plain.seed, 0, flat, plain.grad.sigma, kind=gen.KIND_GRAD_FULL))
+    half = replace(base, grad_shard="fp16")
+    rows, _ = oracle_pool.chunk_inputs(half, flat)
+    g16 = oracle_pool.chunk_gradient(half, rows)
+    assert np.array_equal(g16, ored.reduce_values(rows, half.nd).astype(np.float16)
+                          .view(np.uint16))
