@@ -266,14 +266,11 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # Wait for a quiet device.  The driver clears freed device memory in the
-    # background: after a process frees tens of GB (the previous run's exit
-    # does), concurrent kernels stream 1-5% slower for a few seconds.  Before
-    # the warm-ups, a read of the workload's own resident data is repeated
-    # until its rate has not risen for a second.
+    # Wait for a quiet device (the driver clears freed device memory in the
+    # background, which slows concurrent kernels for seconds).
     settle = None if args.no_settle else settle_device(
         torch, stream, buckets[max(range(len(buckets)), key=lambda i: buckets[i][1])][2]
-        if buckets else grad.view(1, -1))
+        if buckets else live.master)
 
     # Python's cyclic garbage collector stays off from the warm-up to the end of
     # the timed steps: a full collection takes tens of milliseconds on the host,
@@ -438,38 +435,79 @@ def fill_param_shards(sdev, gen, w, shards):
                                 rank0=k, kind=gen.KIND_PARAM16)
 
 
-def settle_device(torch, stream, rows, quiet_s=1.0, max_s=12.0, period_s=0.1):
-    """Repeat a read of `rows` (a [n, cols] int16 view, the workload's own resident
-    data) until its rate has not risen by more than 0.3% for `quiet_s` seconds,
-    or for at most `max_s`.  Returns the wait and the first and best rates."""
+def memory_busy_percent():
+    """The memory controller's busy percentage the driver reports in sysfs, the
+    highest over the cards that expose it, or None where none does."""
+    import glob
+    vals = []
+    for path in glob.glob("/sys/class/drm/card*/device/mem_busy_percent"):
+        try:
+            with open(path) as f:
+                vals.append(int(f.read().strip()))
+        except (OSError, ValueError):
+            pass
+    return max(vals) if vals else None
+
+
+def settle_device(torch, stream, data, quiet_s=1.0, max_s=30.0, period_s=0.1):
+    """Wait, before the warm-ups, until nothing else moves data on the device.
+
+    The driver clears freed device memory in the background; after a process
+    frees tens of GB (the previous run's exit does), concurrent kernels stream
+    1-5% slower for seconds.  First, with this process idle, the memory
+    controller's busy percentage (sysfs mem_busy_percent) must read 0 for half
+    a second.  Then untimed reads of `data` (the workload's own resident data,
+    read as 64 or more rows) run back to back, timed in batches of about 20 GB,
+    until the rate has not risen by more than 0.3% for `quiet_s` seconds; the
+    device is then busy and clocked up when the warm-ups start.  Both waits
+    stop at `max_s`."""
     from synth import probe
-    cols = rows.shape[1] // 8 * 8
-    view = rows[:, :cols]
-    with torch.cuda.stream(stream):
-        sink = torch.zeros(1, dtype=torch.int32, device=rows.device)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    nbytes = 2 * view.shape[0] * cols
     t0 = time.perf_counter()
-    rates, best, t_best = [], 0.0, t0
-    while True:
+    idle_reads, busy_seen = 0, []
+    while time.perf_counter() - t0 < max_s:
+        b = memory_busy_percent()
+        if b is None:                      # not exposed here: the read check alone
+            break
+        busy_seen.append(b)
+        idle_reads = idle_reads + 1 if b == 0 else 0
+        if idle_reads >= 5:
+            break
+        time.sleep(period_s)
+    t_idle = time.perf_counter() - t0
+    if data.dim() == 2 and data.dtype == torch.int16:
+        view = data[:, :data.shape[1] // 8 * 8]
+    else:
+        flat = data.view(torch.int16)
+        cols = flat.numel() // 64 // 8 * 8
+        view = flat[:64 * cols].view(64, cols)
+    with torch.cuda.stream(stream):
+        sink = torch.zeros(1, dtype=torch.int32, device=data.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    nbytes = 2 * view.shape[0] * view.shape[1]
+    reps = max(1, int(2e10 // nbytes))     # about 20 GB (3 ms) per timed batch
+    t1 = time.perf_counter()
+    rates, best, t_best = [], 0.0, t1
+    while True:                            # back to back: the device stays busy
         with torch.cuda.stream(stream):
             ev[0].record(stream)
-            for _ in range(3):
+            for _ in range(reps):
                 probe.read_rows(view, sink, 8, stream=stream)
             ev[1].record(stream)
         torch.cuda.synchronize()
-        r = 3 * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+        r = reps * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
         rates.append(r)
         now = time.perf_counter()
         if r > best * 1.003:
             best, t_best = r, now
-        if now - t_best >= quiet_s or now - t0 >= max_s:
+        if now - t_best >= quiet_s or now - t1 >= max_s:
             break
-        time.sleep(period_s)
-    return {"seconds": time.perf_counter() - t0, "reads": len(rates), "first_gbs": rates[0],
-            "best_gbs": best, "what": "untimed reads of the workload's resident data before the "
-                                      "warm-ups, until the rate stops rising (the driver clears "
-                                      "freed device memory in the background)"}
+    return {"seconds": time.perf_counter() - t0, "memory_idle_wait_s": t_idle,
+            "memory_busy_max": max((b for b in busy_seen if b is not None), default=None),
+            "reads": len(rates), "first_gbs": rates[0], "best_gbs": best,
+            "what": "before the warm-ups: wait until the driver reports the memory controller "
+                    "idle, then read the workload's resident data back to back, untimed, until "
+                    "the rate stops rising (the driver clears freed device memory in the "
+                    "background)"}
 
 
 def stream_ceilings(torch, dev, stream, rows=None, nbytes=4 << 30, reps=10):
