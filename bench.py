@@ -572,8 +572,19 @@ def environment(torch, dev):
             "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
             "hip": torch.version.hip, "torch": torch.__version__,
             "numpy": np.__version__, "host_cpus": len(os.sched_getaffinity(0)),
+            "rocm": read_text("/opt/rocm/.info/version"),
+            "amdgpu_driver": read_text("/sys/module/amdgpu/version"),
             "host_cpu_model": host_cpu_model(),
             "library_sources_sha256": library_sources_sha256()}
+
+
+def read_text(path):
+    """A one-line version file's contents, or None."""
+    try:
+        with open(path) as f:
+            return f.read().strip() or None
+    except OSError:
+        return None
 
 
 def host_cpu_model():

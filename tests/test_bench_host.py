@@ -123,3 +123,30 @@ def test_timed_steps_run_with_the_garbage_collector_off():
     off, warm = main.index("gc.disable()"), main.index("for _ in range(args.warmup):")
     timed, on = main.index("for k in range(args.steps):"), main.index("gc.enable()")
     assert off < warm < timed < on
+
+
+def test_memory_busy_percent_reads_the_busiest_card(tmp_path, monkeypatch):
+    """The quiet-device wait reads the driver's memory-busy counter of every card
+    that exposes one and takes the highest; no such file gives None."""
+    import glob as glob_mod
+    import bench as b
+    for card, val in (("card0", "3\n"), ("card1", "0\n"), ("card2", "junk\n")):
+        d = tmp_path / card / "device"
+        d.mkdir(parents=True)
+        (d / "mem_busy_percent").write_text(val)
+    real = glob_mod.glob
+    monkeypatch.setattr(glob_mod, "glob", lambda pat: real(
+        pat.replace("/sys/class/drm", str(tmp_path))))
+    assert b.memory_busy_percent() == 3
+    (tmp_path / "card0" / "device" / "mem_busy_percent").write_text("0")
+    assert b.memory_busy_percent() == 0
+    monkeypatch.setattr(glob_mod, "glob", lambda pat: [])
+    assert b.memory_busy_percent() is None
+
+
+def test_read_text(tmp_path):
+    import bench as b
+    f = tmp_path / "v"
+    f.write_text("7.2.0\n")
+    assert b.read_text(str(f)) == "7.2.0"
+    assert b.read_text(str(tmp_path / "missing")) is None
