@@ -327,6 +327,16 @@ def main():
             "bytes_per_element": bytes_step / S,
             "gbs": gbs(bytes_step, avg_step), "frac_of_peak": gbs(bytes_step, avg_step) / PEAK_HBM_GBS,
             "params_per_s": S / (avg_step * 1e-3)}
+        traffic = measured_traffic(names[kind], w.name)
+        kernels[kind]["counter_bytes_per_launch"] = traffic
+        kernels[kind]["counter_bytes_per_element"] = (
+            traffic * n_launch / S if traffic is not None else None)
+        kernels[kind]["waves_per_cu_measured"] = measured_waves_per_cu(names[kind], w.name)
+        kernels[kind]["workgroups_per_cu_cap"] = {
+            "reduce": lambda: Z.launch_occupancy(Z.KERNEL_REDUCE_W16)[0],
+            "adam": lambda: Z.launch_occupancy(Z.KERNEL_ADAM_G32 if g_bytes == 4
+                                               else Z.KERNEL_ADAM_G16)[0],
+            "gather": lambda: None}[kind]()
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms_per_step"])
     dk = kernels[dom]
     dom_launch_bytes = dk["bytes_per_step"] / dk["launches_per_step"]
@@ -625,24 +635,40 @@ def kernel_source_sha256(kernel):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel, workload_name, profiles_dir=None):
-    """HBM bytes per launch from the committed counter summary of this kernel and
-    workload, or None when there is none or the kernel source changed since."""
+def profile_fields(kernel, workload_name, profiles_dir=None):
+    """The committed rocprofv3 summary of this kernel and workload, as its "- key:
+    value" fields, or {} when there is none or the kernel source changed since."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(profiles_dir or os.path.join(here, "profiles"),
                         f"{kernel}__{workload_name}.md")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256") != kernel_source_sha256(kernel):
+        return {}
+    return fields
+
+
+def measured_traffic(kernel, workload_name, profiles_dir=None):
+    """HBM bytes per launch from the committed counter summary of this kernel and
+    workload, or None when there is none or the kernel source changed since."""
     try:
-        if fields["kernel source sha256"] != kernel_source_sha256(kernel):
-            return None
-        return int(fields["measured HBM bytes per launch"])
+        return int(profile_fields(kernel, workload_name, profiles_dir)
+                   ["measured HBM bytes per launch"])
     except (KeyError, ValueError):
+        return None
+
+
+def measured_waves_per_cu(kernel, workload_name, profiles_dir=None):
+    """Mean resident waves per CU from the committed occupancy pass, or None."""
+    v = profile_fields(kernel, workload_name, profiles_dir).get("mean waves resident per CU")
+    try:
+        return float(v.split()[0]) if v else None
+    except ValueError:
         return None
 
 
