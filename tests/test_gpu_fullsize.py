@@ -48,7 +48,7 @@ def _host_state(w, flat):
             gen.state_f32(w.seed, gen.KIND_V, flat, w.v.sigma, w.v.absolute))
 
 
-def _reduce_all(w, geom, grad32, chunk=None):
+def _reduce_all(w, geom, grad32, chunk=None, grad16=None):
     """Every bucket that meets the shard, in arrival order; only the owned columns
     arrive (rows at the library's advised stride); the rows are freed after each call.
     Returns the shard-local edges of every bucket and of every chunk launch (each
@@ -65,7 +65,7 @@ def _reduce_all(w, geom, grad32, chunk=None):
             buf = torch.empty(w.nd * stride, dtype=torch.int16, device="cuda")
             rows = buf.as_strided((w.nd, c1 - c0), (stride, 1))
             sdev.fill_grad_rows(rows, w.seed, c0, w.grad.sigma, w.grad.heavy_tail)
-            Z.reduce_shard(geom, c0, c1 - c0, rows, grad32)
+            Z.reduce_shard(geom, c0, c1 - c0, rows, grad32, grad16)
             del rows, buf                                # release
     return edges
 
@@ -148,6 +148,9 @@ def _fullstate(w):
             grad = torch.empty(S, dtype=torch.int16, device="cuda")
             sdev.fill_grad_rows(grad.view(1, S), w.seed, lo, w.grad.sigma, w.grad.heavy_tail,
                                 kind=gen.KIND_GRAD_FULL)
+        elif w.grad_shard == "fp16":
+            grad = torch.zeros(S, dtype=torch.int16, device="cuda")
+            _reduce_all(w, geom, None, grad16=grad)
         else:
             grad = torch.zeros(S, dtype=torch.float32, device="cuda")
             _reduce_all(w, geom, grad)
@@ -162,18 +165,21 @@ def _fullstate(w):
     assert set(want) == {("grad", 0)} | {(n, t) for n in oracle_pool.ARRAYS
                                          for t in range(1, w.steps + 1)}
 
+    half = w.fp16_grad or w.grad_shard == "fp16"
+
     def oracle_grad(j0, n):
         flat = np.arange(lo + j0, lo + j0 + n, dtype=np.uint64)
         if w.fp16_grad:
             return gen.grad_f16(w.seed, 0, flat, w.grad.sigma, w.grad.heavy_tail,
                                 kind=gen.KIND_GRAD_FULL)
-        return _oracle_grad(w, flat)
+        g = _oracle_grad(w, flat)
+        return g.astype(np.float16).view(np.uint16) if half else g
 
     spans_d = dict(spans)
     bad = [j0 for j0, h in sorted(want[("grad", 0)].items()) if got_g[j0] != h]
     if bad:
         j0 = bad[0]
-        assert_bits(g_host[j0:j0 + spans_d[j0]].view(np.uint16 if w.fp16_grad else np.float32),
+        assert_bits(g_host[j0:j0 + spans_d[j0]].view(np.uint16 if half else np.float32),
                     oracle_grad(j0, spans_d[j0]), f"gradient, chunk {j0}")
         pytest.fail(f"gradient digests differ at chunks {bad[:8]}")
     del g_host
@@ -215,6 +221,14 @@ def test_fullstate_zero2_7p5b_rank0():
     """Every element of the 7.5B / Nd = 64 rank-0 shard (117,187,500): the reduced
     fp32 gradient over the five buckets and the state after each of 10 steps."""
     _fullstate(wl.zero2_7p5b(0))
+
+
+@pytest.mark.timeout(900)
+def test_fullstate_zero2_7p5b_fp16_shard():
+    """The same rank with the fp16 gradient shard of the guide's 2 Psi + 14 Psi / Nd
+    accounting: every element of the shard as the reduce rounds it to fp16, and
+    the state after each of 10 steps of Adam on it."""
+    _fullstate(wl.zero2_7p5b_g16(0))
 
 
 @pytest.mark.timeout(900)

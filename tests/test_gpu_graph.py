@@ -141,3 +141,30 @@ def test_captured_stage3_step_replays_equal_eager_steps():
             assert_bits(f32(graphed[key]), f32(eager[key]), f"replay {r} {key}")
         for key in ("grad", "shards", "layer"):
             assert_bits(u16(graphed[key]), u16(eager[key]), f"replay {r} {key}")
+
+
+def test_captured_gather_across_many_shards():
+    """A gather that crosses 37 shards takes three launches (at most 16 pieces
+    each); captured once and replayed, it equals the oracle every time."""
+    from oracle import stage3 as ost3
+    psi, nd, lo, n, replays = 40_000, 37, 5, 39_990, 3
+    s_all = -(-psi // nd)
+    host = np.random.default_rng(5).integers(0, 1 << 16, size=(nd, s_all + 3), dtype=np.uint16)
+    shards = torch.from_numpy(host.view(np.int16)).cuda()
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    Z.gather_params(psi, nd, lo, n, shards, out)            # warm-up, eager
+    torch.cuda.synchronize()
+    want = ost3.gather_params(host, psi, nd, lo, n)
+    assert_bits(u16(out), want, "eager gather")
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    out.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        Z.gather_params(psi, nd, lo, n, shards, out, stream=side)
+    torch.cuda.synchronize()
+    for r in range(replays):
+        out.fill_(0x7E01)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_bits(u16(out), want, f"replay {r}")
