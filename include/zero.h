@@ -53,7 +53,7 @@ extern "C" {
 #define ZERO_E_INVAL (-1)  /* invalid argument: null pointer, Nd = 0, rank >= Nd, bad stage or hyperparameter, geometry mismatch */
 #define ZERO_E_RANGE (-2)  /* a range leaves the parameter vector or a buffer (bucket beyond Psi, stride < length, slot outside the fp16 window) */
 #define ZERO_E_ALIGN (-3)  /* a device pointer is not aligned to its element size */
-#define ZERO_E_DEVICE (-4) /* the HIP runtime reported an error while enqueueing */
+#define ZERO_E_DEVICE (-4) /* the HIP runtime reported an error, or the device cannot hold a streaming kernel to its workgroups-per-CU cap (zero_launch_occupancy) */
 
 /* Stages of zero_memory_model. */
 #define ZERO_STAGE_DP 0     /* plain data parallelism: full replica */
@@ -189,7 +189,8 @@ int zero_row_stride(uint64_t len, uint64_t *stride);
  * ZERO_E_RANGE (bucket beyond psi, slice_stride < bucket_len, size overflow,
  * Nd > 2^24 for a bucket that meets the shard),
  * ZERO_E_ALIGN (slices or grad16 not 2-byte, grad32 not 4-byte aligned),
- * ZERO_E_DEVICE (launch failed).
+ * ZERO_E_DEVICE (launch failed, or the launch's residency cap cannot be set on
+ * this device).
  */
 int zero_reduce_shard(const zero_geom_t *g, uint64_t bucket_offset, uint64_t bucket_len,
                       const uint16_t *slices, uint64_t slice_stride, float *grad32,
@@ -243,7 +244,8 @@ int zero_adam_scalars(double lr, double beta1, double beta2, double eps, uint64_
  * rank's contribution to the all-gather of [A, B, C]).
  * Errors: ZERO_E_INVAL (null pointer, bad geometry or hyperparameter),
  * ZERO_E_RANGE (slot outside the fp16 window), ZERO_E_ALIGN (fp32 arrays not
- * 4-byte, fp16 arrays not 2-byte aligned), ZERO_E_DEVICE (launch failed).
+ * 4-byte, fp16 arrays not 2-byte aligned), ZERO_E_DEVICE (launch failed, or the
+ * launch's residency cap cannot be set on this device).
  */
 int zero_adam_step_shard(const zero_geom_t *g, const zero_shard_t *s, double lr, double beta1,
                          double beta2, double eps, uint64_t step, void *hip_stream);
