@@ -31,6 +31,8 @@
 //
 // Vector width: 16 bytes when a piece's source and destination are 16-byte
 // aligned relative to each other, else 8 or 4 bytes, else element by element.
+// The index plan (pieces, launches, each workgroup's piece) is in
+// gather_plan.h, shared with a CPU check of the kernel's indexing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,48 +41,8 @@
 namespace zero {
 namespace {
 
-constexpr int kThreads = 64;        // one wavefront per workgroup
-constexpr uintptr_t kLine = 128;    // bytes per cache line
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// How one piece of n elements from src to dst is copied: `width` bytes per
-// access, `head` loose elements until dst reaches a line, then `nvec`
-// accesses, then the loose tail; `wgs` workgroups.  Host and device both call
-// it on the same addresses, so they agree on the workgroup count.
-struct Plan {
-  uint32_t width;
-  uint64_t head, nvec, wgs;
-};
-
-__host__ __device__ inline Plan plan_piece(uintptr_t src, uintptr_t dst, uint64_t n) {
-  Plan p;
-  const uintptr_t rel = src - dst;
-  p.width = (rel % 16 == 0) ? 16 : (rel % 8 == 0) ? 8 : (rel % 4 == 0) ? 4 : 2;
-  if (p.width == 2) {
-    p.head = 0;
-    p.nvec = n;
-  } else {
-    uint64_t head = ((kLine - dst % kLine) % kLine) / 2;
-    if (head > n) head = n;
-    p.head = head;
-    p.nvec = (n - head) / (p.width / 2);
-  }
-  const uint64_t w = (p.nvec + kThreads - 1) / kThreads;
-  p.wgs = w ? w : 1;
-  return p;
-}
-
-struct Args {
-  const uint16_t* shards;  // row k at shards + k * stride holds flat [k s, (k + 1) s)
-  uint64_t stride, s;
-  uint64_t lo, end;        // this launch's flat range
-  uint16_t* out;           // out[j] receives flat out_origin + j
-  uint64_t out_origin;
-  uint64_t k_first;        // the row of the launch's first piece
-  uint32_t block0[kMaxGatherPieces];  // first workgroup of each piece; unused: ~0u
-};
 
 template <typename VT>
 __device__ __forceinline__ void copy_vec(const uint16_t* src, uint16_t* dst, uint64_t e) {
@@ -88,38 +50,28 @@ __device__ __forceinline__ void copy_vec(const uint16_t* src, uint16_t* dst, uin
                               reinterpret_cast<VT*>(dst + e));
 }
 
-__global__ void __launch_bounds__(kThreads) copy_kernel(Args a) {
-  uint32_t q = 0;                                      // this workgroup's piece
-#pragma unroll
-  for (uint32_t i = 1; i < kMaxGatherPieces; ++i) q += blockIdx.x >= a.block0[i] ? 1u : 0u;
-  const uint64_t k = a.k_first + q;
-  const uint64_t base = k * a.s;
-  const uint64_t p_lo = base > a.lo ? base : a.lo;
-  const uint64_t p_hi = a.end - base > a.s ? base + a.s : a.end;
-  const uint16_t* src = a.shards + k * a.stride + (p_lo - base);
-  uint16_t* dst = a.out + (p_lo - a.out_origin);
-  const uint64_t n = p_hi - p_lo;
-  const Plan pl = plan_piece(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst), n);
-  const uint64_t wg = blockIdx.x - a.block0[q];
-  const uint64_t v = wg * kThreads + threadIdx.x;
+__global__ void __launch_bounds__(kGatherThreads) copy_kernel(GatherArgs a) {
+  const GatherPiece pc = gather_piece(a, blockIdx.x);
+  const GatherPlan& pl = pc.pl;
+  const uint64_t v = pc.wg * kGatherThreads + threadIdx.x;
   const uint32_t per = pl.width / 2;                   // elements per access
   if (v < pl.nvec) {
     const uint64_t e = pl.head + v * per;
     switch (pl.width) {
-      case 16: copy_vec<u32x4>(src, dst, e); break;
-      case 8: copy_vec<u32x2>(src, dst, e); break;
-      case 4: copy_vec<uint32_t>(src, dst, e); break;
-      default: dst[e] = src[e]; break;
+      case 16: copy_vec<u32x4>(pc.src, pc.dst, e); break;
+      case 8: copy_vec<u32x2>(pc.src, pc.dst, e); break;
+      case 4: copy_vec<uint32_t>(pc.src, pc.dst, e); break;
+      default: pc.dst[e] = pc.src[e]; break;
     }
   }
   // the loose elements, by the piece's last workgroup: the head before the
   // line and the tail after the last full access
-  if (wg + 1 == pl.wgs) {
+  if (pc.wg + 1 == pl.wgs) {
     const uint64_t tail0 = pl.head + pl.nvec * per;
-    const uint64_t loose = pl.head + (n - tail0);
-    for (uint64_t r = threadIdx.x; r < loose; r += kThreads) {
+    const uint64_t loose = pl.head + (pc.n - tail0);
+    for (uint64_t r = threadIdx.x; r < loose; r += kGatherThreads) {
       const uint64_t e = r < pl.head ? r : tail0 + (r - pl.head);
-      dst[e] = src[e];
+      pc.dst[e] = pc.src[e];
     }
   }
 }
@@ -128,38 +80,17 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(Args a) {
 
 hipError_t launch_gather(const GatherLaunch& g, hipStream_t stream) {
   if (g.n == 0) return hipSuccess;
-  const uint64_t end = g.lo + g.n;                     // <= psi: checked by the caller
-  const uint64_t k_last = (end - 1) / g.s;
+  const uint64_t k_last = (g.lo + g.n - 1) / g.s;
   uint64_t k = g.lo / g.s;
   while (k <= k_last) {
-    Args a;
-    a.shards = g.shards;
-    a.stride = g.stride;
-    a.s = g.s;
-    a.out = g.out;
-    a.out_origin = g.lo;
-    a.k_first = k;
-    a.lo = k * g.s > g.lo ? k * g.s : g.lo;
-    uint64_t blocks = 0, p_hi = a.lo;
-    uint32_t q = 0;
-    for (; q < kMaxGatherPieces && k + q <= k_last; ++q) {
-      const uint64_t base = (k + q) * g.s;             // <= end - 1: no overflow
-      const uint64_t p_lo = base > g.lo ? base : g.lo;
-      p_hi = end - base > g.s ? base + g.s : end;
-      const uint16_t* src = g.shards + (k + q) * g.stride + (p_lo - base);
-      const uint16_t* dst = g.out + (p_lo - g.lo);
-      a.block0[q] = static_cast<uint32_t>(blocks);
-      blocks += plan_piece(reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(dst),
-                           p_hi - p_lo).wgs;
-      if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    }
-    for (uint32_t i = q; i < kMaxGatherPieces; ++i) a.block0[i] = ~0u;
-    a.end = p_hi;
-    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                       a);
+    GatherArgs a;
+    uint64_t blocks = 0;
+    k = gather_launch(g, k, &a, &blocks);
+    if (blocks == 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGatherThreads), 0,
+                       stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k += q;
   }
   return hipSuccess;
 }

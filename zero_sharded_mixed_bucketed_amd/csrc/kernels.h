@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gather_plan.h"
+
 namespace zero {
 
 // One bucket (or chunk) of the owner's reduce.  Slice columns c in
@@ -32,20 +34,6 @@ struct AdamLaunch {
   uint64_t n;
   float b1, b2, c1, c2, eps, step, isb;
 };
-
-// The parameters of flat [lo, lo + n) gathered from the rank shards: row k at
-// shards + k * stride holds flat [k * s, (k + 1) * s).
-struct GatherLaunch {
-  const uint16_t* shards;
-  uint64_t stride;
-  uint64_t s;
-  uint64_t lo, n;
-  uint16_t* out;
-};
-
-// Pieces (rank shards crossed) per gather launch; a gather that crosses more
-// shards takes several launches.
-constexpr uint64_t kMaxGatherPieces = 16;
 
 // Workgroup size and the cap on resident workgroups per compute unit of the
 // two streaming kernels.  The cap is set with dynamic LDS that the kernels do
