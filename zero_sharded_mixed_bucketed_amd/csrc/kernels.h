@@ -6,21 +6,9 @@
 #include <stdint.h>
 
 #include "gather_plan.h"
+#include "reduce_plan.h"
 
 namespace zero {
-
-// One bucket (or chunk) of the owner's reduce.  Slice columns c in
-// [c_lo, c_hi) are reduced; output element of column c is out32[c + delta].
-struct ReduceLaunch {
-  const uint16_t* rows;  // row k at rows + k * stride
-  uint64_t stride;
-  uint32_t nd;
-  uint64_t c_lo, c_hi;
-  int64_t delta;
-  float* out32;     // nullable (not both)
-  uint16_t* out16;  // nullable
-  float inv_nd;
-};
 
 // One Adam step over n elements.  p16 (nullable) points at the slot of
 // element 0 in the fp16 parameter window.

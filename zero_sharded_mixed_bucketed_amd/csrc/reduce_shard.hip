@@ -38,7 +38,7 @@ namespace zero {
 namespace {
 
 constexpr int kThreads = kReduceThreads;  // one wavefront per workgroup
-constexpr int kCols = 8;                  // columns per thread (one 16-byte fp16 load per row)
+constexpr int kCols = kReduceCols;        // columns per thread (one 16-byte fp16 load per row)
 constexpr int kBatch = 16;                // rows per batch
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -65,20 +65,7 @@ __device__ __forceinline__ void add8(float (&acc)[kCols], u32x4 x) {
   acc[7] = acc[7] + h2f(x.w >> 16);
 }
 
-struct Args {
-  const uint16_t* rows;
-  uint64_t stride;
-  uint32_t nd;
-  uint64_t col0;     // first column of group 0 (a multiple of 8)
-  uint64_t ngroups;  // groups of 8 columns
-  uint64_t c_lo, c_hi;
-  int64_t delta;
-  float* out32;
-  uint16_t* out16;
-  float inv;
-  int st32;      // 4: 16-byte stores, 2: 8-byte, 1: 4-byte
-  int st16;      // 8: 16-byte stores, 4: 8-byte, 2: 4-byte, 1: 2-byte
-};
+using Args = ReduceArgs;
 
 __device__ __forceinline__ void store_full(const Args& a, uint64_t o, const float (&r)[kCols]) {
   if (a.out32) {
@@ -160,12 +147,13 @@ template <int kW>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(Args a) {
   const uint64_t gi = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (gi >= a.ngroups) return;
-  const uint64_t c = a.col0 + gi * kCols;
+  uint64_t c;
+  const bool full = reduce_group(a, gi, &c);
   float acc[kCols];
 #pragma unroll
   for (int e = 0; e < kCols; ++e) acc[e] = 0.0f;  // +0
 
-  if (c >= a.c_lo && c + kCols <= a.c_hi) {
+  if (full) {
     const uint16_t* p = a.rows + c;
     uint32_t k = 0;
     // The bound is computed once: with it the compiler knows the trip count and
@@ -220,36 +208,10 @@ const void* reduce_kernel_fn(int width) {
 }
 
 hipError_t launch_reduce(const ReduceLaunch& L, const DeviceCaps& d, hipStream_t stream) {
-  Args a;
-  a.rows = L.rows;
-  a.stride = L.stride;
-  a.nd = L.nd;
-  a.c_lo = L.c_lo;
-  a.c_hi = L.c_hi;
-  a.col0 = L.c_lo & ~static_cast<uint64_t>(kCols - 1);
-  a.ngroups = (L.c_hi - a.col0 + kCols - 1) / kCols;
-  a.delta = L.delta;
-  a.out32 = L.out32;
-  a.out16 = L.out16;
-  a.inv = L.inv_nd;
-  // Widest access every row start allows: columns of a group start at a
-  // multiple of 8 elements (16 bytes) from the row start.
-  const uintptr_t ra = reinterpret_cast<uintptr_t>(L.rows) | (2 * L.stride) | 16;
-  const int w = static_cast<int>(ra & (~ra + 1));   // lowest set bit, at most 16
-  // Alignment of the output addresses of full groups: column col0 + 8j maps to
-  // out32 + col0 + delta + 8j, so the alignment class is the same for all.
-  const uint64_t o0 = a.col0 + static_cast<uint64_t>(a.delta);
-  a.st32 = 1;
-  if (L.out32) {
-    const uintptr_t b32 = reinterpret_cast<uintptr_t>(L.out32) + 4 * o0;
-    a.st32 = (b32 % 16 == 0) ? 4 : (b32 % 8 == 0) ? 2 : 1;
-  }
-  a.st16 = 1;
-  if (L.out16) {
-    const uintptr_t b16 = reinterpret_cast<uintptr_t>(L.out16) + 2 * o0;
-    a.st16 = (b16 % 16 == 0) ? 8 : (b16 % 8 == 0) ? 4 : (b16 % 4 == 0) ? 2 : 1;
-  }
-  const uint64_t blocks = (a.ngroups + kThreads - 1) / kThreads;
+  int w = 0;
+  uint64_t groups = 0;
+  const Args a = reduce_plan(L, &w, &groups);
+  const uint64_t blocks = (groups + kThreads - 1) / kThreads;
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   // the dynamic LDS that caps each instantiation at kReduceWgsPerCu per CU
