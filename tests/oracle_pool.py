@@ -18,6 +18,7 @@ from __future__ import annotations
 import hashlib
 import multiprocessing as mp
 import os
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -93,11 +94,28 @@ class ShardOracle:
         self.chunks = chunks(length, chunk)
         jobs = [(w, offset, j0, n, steps) for j0, n in self.chunks]
         self._pool = mp.get_context("spawn").Pool(workers())
-        self._res = self._pool.map_async(chunk_trajectory, jobs, chunksize=1)
+        self._it = self._pool.imap_unordered(chunk_trajectory, jobs, chunksize=1)
 
-    def result(self, timeout: float = 900.0):
+    def result(self, timeout: float = 900.0, progress_s: float = 20.0):
+        """Waits for every chunk, printing how many are done every `progress_s`
+        seconds (a whole shard takes minutes); raises TimeoutError after
+        `timeout` seconds."""
+        n = len(self.chunks)
+        parts = []
+        t0 = last = time.monotonic()
         try:
-            parts = self._res.get(timeout)
+            while len(parts) < n:
+                try:
+                    parts.append(self._it.next(timeout=1.0))
+                except mp.TimeoutError:
+                    pass
+                now = time.monotonic()
+                if now - t0 > timeout:
+                    raise TimeoutError(f"oracle pool: {len(parts)} of {n} chunks after "
+                                       f"{timeout:.0f} s")
+                if now - last >= progress_s:
+                    print(f"oracle pool: {len(parts)} of {n} chunks done", flush=True)
+                    last = now
         finally:
             self._pool.terminate()
             self._pool.join()
