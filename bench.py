@@ -629,10 +629,20 @@ KERNEL_SOURCES = {"reduce_kernel": "reduce_shard.hip", "adam_vec_kernel": "adam_
 
 
 def kernel_source_sha256(kernel):
+    """One digest over the kernel's HIP source and the library's internal headers
+    that every kernel source compiles (csrc/*.h: launch constants and the index
+    plans), each file's name then its bytes: a profile recorded under another
+    digest was taken from other code."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "zero_sharded_mixed_bucketed_amd", "csrc", KERNEL_SOURCES[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    csrc = os.path.join(here, "zero_sharded_mixed_bucketed_amd", "csrc")
+    paths = [os.path.join(csrc, KERNEL_SOURCES[kernel])]
+    paths += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith(".h")]
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def profile_fields(kernel, workload_name, profiles_dir=None):

@@ -63,8 +63,29 @@ def test_traffic_lookup_rules(tmp_path):
     assert b.measured_traffic("reduce_kernel", "w2", d) is None
     _summary(d, "adam_vec_kernel", "w1", sha, 99)                        # another kernel's source
     assert b.measured_traffic("adam_vec_kernel", "w1", d) is None
-    assert sha == hashlib.sha256(open(os.path.join(
-        ROOT, "zero_sharded_mixed_bucketed_amd", "csrc", "reduce_shard.hip"), "rb").read()).hexdigest()
+    # the digest covers the kernel's source and the internal headers it compiles
+    csrc = os.path.join(ROOT, "zero_sharded_mixed_bucketed_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ["reduce_shard.hip"] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    assert sha == h.hexdigest()
+    assert {"kernels.h", "reduce_plan.h", "gather_plan.h"} <= set(os.listdir(csrc))
+
+
+def test_committed_summaries_match_the_current_sources():
+    """Every committed rocprofv3 summary was taken from the kernel sources and
+    headers as they stand, so the counter bytes the bench reports from it
+    describe the code that runs."""
+    b = _bench()
+    pdir = os.path.join(ROOT, "profiles")
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith(".md"):
+            continue
+        kernel = f[:-3].split("__")[0]
+        m = re.search(r"^- kernel source sha256: `([0-9a-f]{64})`$",
+                      open(os.path.join(pdir, f)).read(), re.M)
+        assert m and m.group(1) == b.kernel_source_sha256(kernel), f
 
 
 def test_committed_summaries_are_well_formed():
